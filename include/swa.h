@@ -1,0 +1,266 @@
+/*
+ * swa.h -- C ABI of the MI355X (gfx950) frame-block sliding-window attention
+ * library over a streaming, paged KV cache.
+ *
+ * Sources of the semantics (cited by page title and section):
+ *  [G]  "Sliding Window Attention Mechanism in AggregatorStream:
+ *       Implementation and Configuration Guide" (instagit.com): sections
+ *       "Mask Generation in CausalAttention", "KV Cache Eviction Strategy",
+ *       "Manual Sliding-Window Mask Construction", "Cache Reset Between
+ *       Sequences", FAQ.
+ *  [IO] "Stream.py Aggregator Input and Output Formats: A Complete Technical
+ *       Guide" (instagit.com): "Input Tensor Specifications", "Positional
+ *       Embeddings" (3-D RoPE).
+ *  [EX] the sliding-window-attention explainer (akshathtiwari.co.in): the
+ *       rolling buffer written at slot i modulo W.
+ *  [FB] codehub.bot symbol page of FlashInferBlock.forward: the streaming
+ *       branch (keyframe: append_frame, evict_frames, compute_attention;
+ *       non-keyframe: append with eviction deferred, compute_attention,
+ *       rollback_last_frame).
+ *
+ * Conventions for every entry point:
+ *  - Return 0 (SWA_OK) or a negative SWA_E_* code; nothing is thrown across
+ *    the ABI.  swa_last_error() gives a thread-local message for the last
+ *    failure on the calling thread.
+ *  - Device pointers are caller-owned and must stay valid until the work
+ *    enqueued on `stream` has finished.  Host pointers are read or written
+ *    before the call returns.
+ *  - Token tensors are contiguous NHD: [tokens, H, D] with D fastest, in the
+ *    element type named by `dtype` (SWA_BF16 = bfloat16, SWA_F32 = float).
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    null stream).  Ring bookkeeping is done on the host at enqueue time, so
+ *    state errors are reported without reading the device.
+ *  - A cache handle is not thread-safe.  Batch size is 1 per call.
+ *  - No entry point allocates device memory.
+ */
+#ifndef SWA_H
+#define SWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. */
+typedef struct ihipStream_t* swa_stream_t;
+
+enum swa_status {
+    SWA_OK = 0,
+    SWA_E_INVAL = -1,        /* bad argument or config                        */
+    SWA_E_STATE = -2,        /* call not allowed in the cache's current state */
+    SWA_E_CAPACITY = -3,     /* window off and max_frames keyframes cached    */
+    SWA_E_UNSUPPORTED = -4,  /* valid but not implemented (e.g. head_dim 48)  */
+    SWA_E_HIP = -5           /* a HIP runtime call or launch failed           */
+};
+
+enum swa_dtype { SWA_BF16 = 0, SWA_F32 = 1 };
+
+enum swa_region { SWA_REGION_FRAME = 0, SWA_REGION_SPECIAL = 1 };
+
+/*
+ * Cache configuration ([G] constructor arguments; [FB] evict_frames
+ * arguments).
+ *   tokens_per_frame P     patch + special tokens per frame ([IO]).
+ *   head_dim D             32 or 64.
+ *   sliding_window_size    in blocks; -1 switches the window off ([G] FAQ);
+ *                          0 and values below -1 are rejected.
+ *   num_frame_per_block    window length in frames is
+ *                          W = sliding_window_size * num_frame_per_block
+ *                          ([G] "Mask Generation in CausalAttention").
+ *   scale_frames S         the first S keyframes are never evicted ([G]
+ *                          "KV Cache Eviction Strategy").  S = 0 is the
+ *                          include_scale_frames = false case.
+ *   cross_frame_special    keep `special_rows` rows (starting at row
+ *                          `special_row0` of each frame) of every evicted
+ *                          frame ([G] eviction section and FAQ), for at most
+ *                          `max_special_frames` (R) evicted frames, oldest
+ *                          dropped first.  camera_only is special_rows = 1.
+ *   max_frames             capacity in keyframes when the window is off.
+ *   rope_pairs_t/h/w, rope_theta
+ *                          3-D RoPE bands used by swa_stream_step when a
+ *                          position array is given ([IO] "Positional
+ *                          Embeddings"); pairs must add up to D/2.
+ */
+typedef struct swa_config {
+    int32_t num_layers;
+    int32_t tokens_per_frame;
+    int32_t num_heads;
+    int32_t head_dim;
+    int32_t dtype;
+    int32_t sliding_window_size;
+    int32_t num_frame_per_block;
+    int32_t scale_frames;
+    int32_t cross_frame_special;
+    int32_t special_row0;
+    int32_t special_rows;
+    int32_t max_special_frames;
+    int32_t max_frames;
+    int32_t rope_pairs_t;
+    int32_t rope_pairs_h;
+    int32_t rope_pairs_w;
+    float rope_theta;
+} swa_config;
+
+/*
+ * One record of a visible-page list, in key order: scale frames, retained
+ * special rows (oldest evicted frame first), window frames, then a pending
+ * non-keyframe.  region SWA_REGION_FRAME: `slot` is the page slot, row0 = 0,
+ * nrows = P.  region SWA_REGION_SPECIAL: `slot` is the special-ring entry
+ * (push index mod R), row0 = slot * special_rows, nrows = special_rows.
+ */
+typedef struct swa_page {
+    int32_t frame;
+    int32_t region;
+    int32_t slot;
+    int32_t row0;
+    int32_t nrows;
+} swa_page;
+
+/*
+ * Where the cache keeps its rows inside the caller's pool (bytes from the
+ * pool base).  Per layer l, with E = element size:
+ *   K   at k_offset + l*layer_bytes, laid out [H][rows][D]
+ *   V^T at v_offset + l*layer_bytes, laid out [H][D][rows]
+ * Page slot s holds a frame in rows [s*P, (s+1)*P); special-ring entry e
+ * holds its rows at special_row_base + e*special_rows.
+ */
+typedef struct swa_layout {
+    int64_t layer_bytes;
+    int64_t k_offset;
+    int64_t v_offset;
+    int64_t meta_offset;
+    int64_t work_offset;
+    int64_t work_bytes;
+    int32_t rows;
+    int32_t num_slots;
+    int32_t special_row_base;
+    int32_t elem_bytes;
+    int32_t window_frames;    /* -1 when the window is off */
+    int32_t scratch_slot;
+} swa_layout;
+
+typedef struct swa_cache swa_cache;
+
+/* Bytes of device memory a cache with this config needs (0 if invalid). */
+size_t swa_cache_pool_bytes(const swa_config* cfg);
+
+/*
+ * Create a cache over a caller-owned device pool of at least
+ * swa_cache_pool_bytes(cfg) bytes (256-byte aligned).  The library owns only
+ * host-side bookkeeping.  dev_pool = NULL with pool_bytes = 0 makes a
+ * bookkeeping-only cache: append/evict/rollback/reset and
+ * kvcache_visible_pages work and enqueue nothing; every call that would touch
+ * the device returns SWA_E_STATE.
+ */
+int swa_cache_create(const swa_config* cfg, void* dev_pool, size_t pool_bytes, swa_cache** out);
+int swa_cache_destroy(swa_cache* cache);
+int swa_cache_layout(const swa_cache* cache, swa_layout* out);
+
+/* KV splits used by the streaming attention (0 = automatic, else 1..32). */
+int swa_cache_set_splits(swa_cache* cache, int splits);
+
+/* Forget every cached frame of every layer ([G] "Cache Reset Between
+ * Sequences": clean_kv_cache).  Host bookkeeping only; nothing enqueued. */
+int kvcache_reset(swa_cache* cache, swa_stream_t stream);
+
+/*
+ * append_frame ([FB]).  k, v: device [P, H, D].  frame_t must exceed every
+ * frame index appended to this layer since the last reset.
+ * keyframe != 0: the frame takes keyframe ordinal n; slot n if n < S, else
+ *   S + ((n - S) mod W) -- the rolling buffer of [EX], shifted past the
+ *   scale slots.  When the window is full this overwrites the slot of the
+ *   frame the following kvcache_evict drops; with cross_frame_special that
+ *   frame's special rows are copied to the special ring first.
+ *   SWA_E_STATE if an eviction is pending or a non-keyframe is pending.
+ * keyframe == 0: the frame goes to the scratch slot with eviction deferred;
+ *   it must be removed with kvcache_rollback before the next append.
+ * With the window off: SWA_E_CAPACITY once max_frames keyframes are cached.
+ */
+int kvcache_append(swa_cache* cache, int layer, int64_t frame_t, const void* k, const void* v,
+                   int keyframe, swa_stream_t stream);
+
+/* evict_frames ([FB]; rule of [G] "KV Cache Eviction Strategy"): when more
+ * than W + S keyframes are cached, drop cached positions [S, n_cached - W).
+ * No-op with the window off or while a non-keyframe is pending (eviction
+ * deferred).  Host bookkeeping only. */
+int kvcache_evict(swa_cache* cache, int layer, swa_stream_t stream);
+
+/* rollback_last_frame ([FB]): drop the pending non-keyframe.  SWA_E_STATE if
+ * there is none.  Host bookkeeping only. */
+int kvcache_rollback(swa_cache* cache, int layer, swa_stream_t stream);
+
+/* compute_attention ([FB]): attention of q (device [P, H, D]) over every
+ * visible row of the layer -- scale frames, retained special rows, window
+ * frames and a pending non-keyframe -- with softmax scale 1/sqrt(D).  Writes
+ * out (device [P, H, D]) and, if not NULL, lse (device float [H, P]).
+ * SWA_E_STATE if nothing is cached. */
+int kvcache_attend(swa_cache* cache, int layer, const void* q, void* out, float* lse, swa_stream_t stream);
+
+/* Host copy of the layer's visible-page list (records in key order).  Writes
+ * min(n, cap) records to `out` and the full count to *n_out. */
+int kvcache_visible_pages(const swa_cache* cache, int layer, swa_page* out, int cap, int* n_out);
+
+/* The same list built on the device from the device-side frame tables (the
+ * page-list builder kernel), copied back; synchronises `stream`. */
+int kvcache_read_device_pages(swa_cache* cache, int layer, swa_page* host_out, int cap, int* n_out,
+                              swa_stream_t stream);
+
+/*
+ * 3-D RoPE in place on q and k, device [n_tokens, H, D] ([IO] "Positional
+ * Embeddings": head_dim/2 complex values).  Pair p = (x[2p], x[2p+1]).
+ * Pairs [0, pairs_t) use pos_thw[n*3+0], the next pairs_h use [n*3+1], the
+ * last pairs_w use [n*3+2]; local pair kk of a band with d_b pairs turns by
+ * pos * theta^(-kk/d_b) radians.  pos_thw: device int32 [n_tokens, 3].
+ * Either q or k may be NULL.
+ */
+int rope3d_apply(void* q, void* k, const int32_t* pos_thw, int n_tokens, int H, int D, int pairs_t,
+                 int pairs_h, int pairs_w, float theta, int dtype, swa_stream_t stream);
+
+/*
+ * One streaming step of one layer ([FB] streaming branch).
+ * keyframe:     [rope] -> append -> evict -> attend.
+ * non-keyframe: [rope] -> append (eviction deferred) -> attend -> rollback.
+ * q: device [P, H, D]; rotated in place when pos_thw is not NULL.
+ * k, v: device [P, H, D]; not modified (the rotated k goes to the cache).
+ * pos_thw: device int32 [P, 3] or NULL (no RoPE).
+ * out: device [P, H, D] (dtype of the cache); lse: device float [H, P]
+ * (natural log of each row's softmax denominator, scores scaled by
+ * 1/sqrt(D)) or NULL.
+ */
+int swa_stream_step(swa_cache* cache, int layer, int64_t frame_t, void* q, const void* k,
+                    const void* v, const int32_t* pos_thw, int keyframe, void* out, float* lse,
+                    swa_stream_t stream);
+
+/*
+ * Masked prefill of F frames submitted at once ([G] "Mask Generation in
+ * CausalAttention"): query frame i sees key frame j iff j <= i and
+ * (j >= i - W + 1 or j < scale_frames), W = sliding_window_size *
+ * num_frame_per_block (-1: no window).  q, k, v, out: device [F*P, H, D];
+ * lse: device float [H, F*P] or NULL.  bf16 needs a device workspace of
+ * swa_prefill_workspace_bytes() bytes (the frames are re-laid out there);
+ * F32 needs none (pass NULL, 0).
+ */
+size_t swa_prefill_workspace_bytes(int F, int P, int H, int D, int dtype);
+int swa_prefill_masked(const void* q, const void* k, const void* v, int F, int P, int H, int D,
+                       int sliding_window_size, int num_frame_per_block, int scale_frames, int dtype,
+                       void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       swa_stream_t stream);
+
+/*
+ * The prefill visibility as bytes (1 = visible) from the same device
+ * predicate the prefill kernels use: [F, F] if token_level == 0, else
+ * [F*P, F*P].  dev_out: device uint8.
+ */
+int swa_prefill_mask(int F, int P, int sliding_window_size, int num_frame_per_block,
+                     int scale_frames, int token_level, uint8_t* dev_out, swa_stream_t stream);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* swa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H */

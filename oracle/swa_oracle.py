@@ -280,12 +280,12 @@ class NaiveRingCache:
         cfg = self.cfg
         if self.pending is not None:
             raise RingError("a non-keyframe is pending; roll it back first")
-        if self.last_frame is not None and t <= self.last_frame:
-            raise RingError("frame indices must increase")
+        if t < 0 or (self.last_frame is not None and t <= self.last_frame):
+            raise RingError("frame indices must be non-negative and increase")
         W, S = cfg.W, cfg.scale_frames
+        if W is not None and len(self.cached) > S + W:
+            raise RingError("evict before the next append")
         if keyframe:
-            if W is not None and len(self.cached) > S + W:
-                raise RingError("evict before appending another keyframe")
             n = self.n_key
             if W is None:
                 if n >= cfg.max_frames:

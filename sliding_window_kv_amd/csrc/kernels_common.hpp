@@ -1,0 +1,84 @@
+// Shared device helpers for the gfx950 kernels: element types, bf16
+// conversion, the prefill visibility ranges and kernel argument structs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxSegs = 8;      // row segments per streaming attention call
+constexpr int kMaxSplits = 32;   // KV splits of one streaming attention call
+
+__device__ __forceinline__ float bf2f(uint16_t b) {
+    return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+    return static_cast<uint32_t>(f2bf(lo)) | (static_cast<uint32_t>(f2bf(hi)) << 16);
+}
+
+// Visible key frames of query frame i in a masked prefill (guide, "Mask
+// Generation in CausalAttention", with scale frames kept): the scale range
+// A = [0, min(S, i+1)) and the window B = [max(0, i - W + 1), i + 1)
+// (W < 0: no window).  When they touch, A covers both and B is empty.
+__host__ __device__ __forceinline__ void prefill_ranges(int i, int W, int S, int* a0, int* a1,
+                                                         int* b0, int* b1) {
+    const int ws = (W < 0) ? 0 : ((i - W + 1) > 0 ? (i - W + 1) : 0);
+    const int se = (S < i + 1) ? S : (i + 1);
+    const bool merged = ws <= se;
+    *a0 = 0;
+    *a1 = merged ? i + 1 : se;
+    *b0 = merged ? i + 1 : ws;
+    *b1 = i + 1;
+}
+
+__host__ __device__ __forceinline__ bool prefill_visible(int i, int j, int W, int S) {
+    int a0, a1, b0, b1;
+    prefill_ranges(i, W, S, &a0, &a1, &b0, &b1);
+    return (j >= a0 && j < a1) || (j >= b0 && j < b1);
+}
+
+// Row segments in the layer's row space, passed by value.
+struct SegList {
+    int n;
+    int lo[kMaxSegs];
+    int hi[kMaxSegs];
+    int tile0[kMaxSegs];     // first tile index of the segment
+    int total_tiles;
+};
+
+struct AttnParams {
+    const void* q;           // [nq_total, H, D] NHD
+    const void* kreg;        // [H][rows][D]
+    const void* vreg;        // [H][D][rows]  (V transposed)
+    void* out;               // [nq_total, H, D]
+    float* lse;              // [H, nq_total] or null
+    float* part_o;           // [splits][H][nq][D] (split > 1)
+    float* part_ml;          // [splits][H][nq][2]
+    int nq;                  // query rows per frame (P)
+    int H;
+    int rows;                // row length of the K/V regions
+    int splits;
+    int qtiles;              // query tiles per frame
+    float scale_log2;        // log2(e) / sqrt(D)
+    // prefill only
+    int F;
+    int W;
+    int S;
+    int fP;                  // key rows per frame in the region
+    SegList seg;             // streaming only
+};
+
+}  // namespace swa

@@ -1,0 +1,341 @@
+// Data-movement kernels of the frame cache on gfx950: append (with the 3-D
+// RoPE fused in), special-row retention, standalone RoPE, the device
+// page-list builder and the prefill mask export.
+//
+// Cache layout of one layer (rows = the layer's row space):
+//   K   [H][rows][D]  -- a key row is D contiguous elements
+//   V^T [H][D][rows]  -- transposed, so the attention kernel reads 8
+//                        consecutive keys of one feature as one 16-byte load
+// A frame in page slot s owns rows [s*P, (s+1)*P) (guide "KV Cache Eviction
+// Strategy": whole frames enter and leave the cache).
+#include "launch.hpp"
+
+namespace swa {
+
+namespace {
+
+template <typename T>
+struct Elt;
+template <>
+struct Elt<uint16_t> {
+    static constexpr int kPer16B = 8;
+    __device__ static float ld(uint16_t x) { return bf2f(x); }
+    __device__ static uint16_t st(float f) { return f2bf(f); }
+};
+template <>
+struct Elt<float> {
+    static constexpr int kPer16B = 4;
+    __device__ static float ld(float x) { return x; }
+    __device__ static float st(float f) { return f; }
+};
+
+// One 16-byte chunk of elements.
+template <typename T>
+union Chunk {
+    uint4 u;
+    T e[Elt<T>::kPer16B];
+};
+
+// Angle of pair p for a token at position pos (band chosen by p), reduced to
+// [-pi, pi] in double before the single-precision sine and cosine.
+__device__ __forceinline__ void rope_cs(const RopeArgs& r, const int32_t* pos3, int p, float* c,
+                                        float* s) {
+    const int band = p < r.pairs_t ? 0 : (p < r.pairs_t + r.pairs_h ? 1 : 2);
+    const double a = static_cast<double>(pos3[band]) * r.freq[p];
+    const double twopi = 6.283185307179586476925286766559;
+    const double red = a - twopi * rint(a * (1.0 / twopi));
+    sincosf(static_cast<float>(red), s, c);
+}
+
+// Rotate the E elements (E/2 pairs) of one 16-byte chunk in place.
+template <typename T>
+__device__ __forceinline__ void rope_chunk(T* x, const RopeArgs& r, const int32_t* pos3, int p0) {
+    constexpr int E = Elt<T>::kPer16B;
+#pragma unroll
+    for (int j = 0; j < E / 2; ++j) {
+        float c, s;
+        rope_cs(r, pos3, p0 + j, &c, &s);
+        const float a = Elt<T>::ld(x[2 * j]);
+        const float b = Elt<T>::ld(x[2 * j + 1]);
+        x[2 * j] = Elt<T>::st(a * c - b * s);
+        x[2 * j + 1] = Elt<T>::st(a * s + b * c);
+    }
+}
+
+constexpr int kTileRows = 64;
+
+// One block = 64 destination rows (8-aligned) of one head.
+template <typename T, int D, bool ROPE>
+__global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, const T* __restrict__ v,
+                                                     T* __restrict__ kreg, T* __restrict__ vreg,
+                                                     T* __restrict__ q, const int32_t* __restrict__ pos,
+                                                     RopeArgs rope, int H, int n_tok, int row0, int rows,
+                                                     int32_t* meta_slot, int32_t frame_id) {
+    constexpr int E = Elt<T>::kPer16B;
+    constexpr int CPR = D / E;               // 16-byte chunks per row
+    constexpr int LD = D + 2;                // padded LDS row
+    __shared__ T vt[kTileRows * LD];
+
+    const int h = blockIdx.y;
+    const int base = (row0 & ~7) + blockIdx.x * kTileRows;   // first destination row
+    const int tid = threadIdx.x;
+
+    if (meta_slot != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *meta_slot = frame_id;
+
+    for (int c = tid; c < kTileRows * CPR; c += 256) {
+        const int rr = c / CPR;
+        const int ch = c % CPR;
+        const int r = base + rr;
+        const int tok = r - row0;
+        Chunk<T> kv, vv;
+        if (tok >= 0 && tok < n_tok) {
+            const size_t src = (static_cast<size_t>(tok) * H + h) * D + ch * E;
+            kv.u = *reinterpret_cast<const uint4*>(k + src);
+            vv.u = *reinterpret_cast<const uint4*>(v + src);
+            if constexpr (ROPE) {
+                const int32_t* p3 = pos + 3 * tok;
+                rope_chunk<T>(kv.e, rope, p3, ch * E / 2);
+                Chunk<T> qv;
+                qv.u = *reinterpret_cast<const uint4*>(q + src);
+                rope_chunk<T>(qv.e, rope, p3, ch * E / 2);
+                *reinterpret_cast<uint4*>(q + src) = qv.u;
+            }
+            *reinterpret_cast<uint4*>(kreg + (static_cast<size_t>(h) * rows + r) * D + ch * E) = kv.u;
+        } else {
+            vv.u = make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) vt[rr * LD + ch * E + e] = vv.e[e];
+    }
+    __syncthreads();
+
+    // Transposed V: E consecutive rows of one feature per 16-byte store.
+    constexpr int KC = kTileRows / E;        // key chunks per feature
+    for (int c = tid; c < D * KC; c += 256) {
+        const int d = c / KC;
+        const int kc = c % KC;
+        const int r = base + kc * E;
+        Chunk<T> out;
+#pragma unroll
+        for (int e = 0; e < E; ++e) out.e[e] = vt[(kc * E + e) * LD + d];
+        T* dst = vreg + (static_cast<size_t>(h) * D + d) * rows + r;
+        const int t0 = r - row0;
+        if (t0 >= 0 && t0 + E <= n_tok) {
+            *reinterpret_cast<uint4*>(dst) = out.u;
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (t0 + e >= 0 && t0 + e < n_tok) dst[e] = out.e[e];
+        }
+    }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void retain_kernel(T* __restrict__ kreg, T* __restrict__ vreg, int rows,
+                                                     int src_row, int dst_row, int ns, int32_t* meta_slot,
+                                                     int32_t frame_id) {
+    const int h = blockIdx.x;
+    if (meta_slot != nullptr && h == 0 && threadIdx.x == 0) *meta_slot = frame_id;
+    T* kh = kreg + static_cast<size_t>(h) * rows * D;
+    for (int i = threadIdx.x; i < ns * D; i += blockDim.x)
+        kh[static_cast<size_t>(dst_row) * D + i] = kh[static_cast<size_t>(src_row) * D + i];
+    T* vh = vreg + static_cast<size_t>(h) * D * rows;
+    for (int i = threadIdx.x; i < ns * D; i += blockDim.x) {
+        const int d = i / ns;
+        const int r = i % ns;
+        vh[static_cast<size_t>(d) * rows + dst_row + r] = vh[static_cast<size_t>(d) * rows + src_row + r];
+    }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ q, T* __restrict__ k,
+                                                   const int32_t* __restrict__ pos, RopeArgs rope,
+                                                   int H, int n_tok) {
+    constexpr int E = Elt<T>::kPer16B;
+    constexpr int CPR = D / E;
+    const int64_t n = static_cast<int64_t>(n_tok) * H * CPR;
+    for (int64_t c = blockIdx.x * 256ll + threadIdx.x; c < n; c += static_cast<int64_t>(gridDim.x) * 256) {
+        const int ch = static_cast<int>(c % CPR);
+        const int tok = static_cast<int>(c / (CPR * H));
+        const int32_t* p3 = pos + 3 * tok;
+        Chunk<T> x;
+        if (q != nullptr) {
+            x.u = *reinterpret_cast<const uint4*>(q + c * E);
+            rope_chunk<T>(x.e, rope, p3, ch * E / 2);
+            *reinterpret_cast<uint4*>(q + c * E) = x.u;
+        }
+        if (k != nullptr) {
+            x.u = *reinterpret_cast<const uint4*>(k + c * E);
+            rope_chunk<T>(x.e, rope, p3, ch * E / 2);
+            *reinterpret_cast<uint4*>(k + c * E) = x.u;
+        }
+    }
+}
+
+// Visible-page list from the device frame tables and the ring counters:
+// scale frames, retained special entries (oldest first), window frames,
+// pending non-keyframe.
+__global__ __launch_bounds__(256) void builder_kernel(BuilderArgs a) {
+    const int sc = a.W < 0 ? static_cast<int>(a.n_key) : static_cast<int>(min<int64_t>(a.n_key, a.S));
+    const int64_t e0 = a.cross ? max<int64_t>(0, a.n_special - a.R) : 0;
+    const int nsp = a.cross ? static_cast<int>(a.n_special - e0) : 0;
+    for (int idx = threadIdx.x; idx < a.total; idx += blockDim.x) {
+        int32_t frame, region, slot, row0, nrows;
+        if (idx < sc) {
+            frame = a.ord_frame[idx];
+            region = 0;
+            slot = idx;
+            row0 = 0;
+            nrows = a.P;
+        } else if (idx < sc + nsp) {
+            const int64_t e = e0 + (idx - sc);
+            frame = a.special_frame[e % (a.R + 1)];
+            region = 1;
+            slot = static_cast<int>(e % a.R);
+            row0 = slot * a.ns;
+            nrows = a.ns;
+        } else if (idx < sc + nsp + a.n_win) {
+            const int64_t o = a.n_key - a.n_win + (idx - sc - nsp);
+            frame = a.ord_frame[a.S + (o - a.S) % (a.W + 1)];
+            region = 0;
+            slot = a.S + static_cast<int>((o - a.S) % a.W);
+            row0 = 0;
+            nrows = a.P;
+        } else {
+            frame = *a.pending_frame;
+            region = 0;
+            slot = a.num_slots - 1;
+            row0 = 0;
+            nrows = a.P;
+        }
+        int32_t* o5 = a.out + 5 * idx;
+        o5[0] = frame;
+        o5[1] = region;
+        o5[2] = slot;
+        o5[3] = row0;
+        o5[4] = nrows;
+    }
+}
+
+__global__ __launch_bounds__(256) void mask_kernel(int F, int P, int W, int S, int token_level,
+                                                   uint8_t* out) {
+    const int64_t n = token_level ? static_cast<int64_t>(F) * P : F;
+    const int64_t total = n * n;
+    for (int64_t x = blockIdx.x * 256ll + threadIdx.x; x < total; x += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t r = x / n;
+        const int64_t c = x % n;
+        const int i = static_cast<int>(token_level ? r / P : r);
+        const int j = static_cast<int>(token_level ? c / P : c);
+        out[x] = prefill_visible(i, j, W, S) ? 1 : 0;
+    }
+}
+
+template <typename T, int D>
+hipError_t append_dispatch(int H, int n_tok, int row0, int rows, const void* k, const void* v,
+                           void* kreg, void* vreg, void* q, const int32_t* pos, const RopeArgs* rope,
+                           int32_t* meta_slot, int32_t frame_id, hipStream_t stream) {
+    const int first = row0 & ~7;
+    const int tiles = (row0 + n_tok - first + kTileRows - 1) / kTileRows;
+    dim3 grid(tiles, H);
+    RopeArgs r{};
+    if (rope != nullptr) r = *rope;
+    if (rope != nullptr)
+        hipLaunchKernelGGL((append_kernel<T, D, true>), grid, dim3(256), 0, stream,
+                           static_cast<const T*>(k), static_cast<const T*>(v), static_cast<T*>(kreg),
+                           static_cast<T*>(vreg), static_cast<T*>(q), pos, r, H, n_tok, row0, rows,
+                           meta_slot, frame_id);
+    else
+        hipLaunchKernelGGL((append_kernel<T, D, false>), grid, dim3(256), 0, stream,
+                           static_cast<const T*>(k), static_cast<const T*>(v), static_cast<T*>(kreg),
+                           static_cast<T*>(vreg), static_cast<T*>(q), pos, r, H, n_tok, row0, rows,
+                           meta_slot, frame_id);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_append(int dtype, int H, int D, int n_tok, int row0, int rows, const void* k,
+                         const void* v, void* kreg, void* vreg, void* q, const int32_t* pos,
+                         const RopeArgs* rope, int32_t* meta_slot, int32_t frame_id,
+                         hipStream_t stream) {
+    if (dtype == 0) {
+        if (D == 64)
+            return append_dispatch<uint16_t, 64>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope,
+                                                 meta_slot, frame_id, stream);
+        return append_dispatch<uint16_t, 32>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope,
+                                             meta_slot, frame_id, stream);
+    }
+    if (D == 64)
+        return append_dispatch<float, 64>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope,
+                                          meta_slot, frame_id, stream);
+    return append_dispatch<float, 32>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, meta_slot,
+                                      frame_id, stream);
+}
+
+hipError_t launch_retain(int dtype, int H, int D, int rows, int src_row, int dst_row, int ns,
+                         void* kreg, void* vreg, int32_t* meta_slot, int32_t frame_id,
+                         hipStream_t stream) {
+    if (dtype == 0) {
+        if (D == 64)
+            hipLaunchKernelGGL((retain_kernel<uint16_t, 64>), dim3(H), dim3(256), 0, stream,
+                               static_cast<uint16_t*>(kreg), static_cast<uint16_t*>(vreg), rows, src_row,
+                               dst_row, ns, meta_slot, frame_id);
+        else
+            hipLaunchKernelGGL((retain_kernel<uint16_t, 32>), dim3(H), dim3(256), 0, stream,
+                               static_cast<uint16_t*>(kreg), static_cast<uint16_t*>(vreg), rows, src_row,
+                               dst_row, ns, meta_slot, frame_id);
+    } else {
+        if (D == 64)
+            hipLaunchKernelGGL((retain_kernel<float, 64>), dim3(H), dim3(256), 0, stream,
+                               static_cast<float*>(kreg), static_cast<float*>(vreg), rows, src_row, dst_row,
+                               ns, meta_slot, frame_id);
+        else
+            hipLaunchKernelGGL((retain_kernel<float, 32>), dim3(H), dim3(256), 0, stream,
+                               static_cast<float*>(kreg), static_cast<float*>(vreg), rows, src_row, dst_row,
+                               ns, meta_slot, frame_id);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_rope(int dtype, int n_tok, int H, int D, void* q, void* k, const int32_t* pos,
+                       const RopeArgs& rope, hipStream_t stream) {
+    const int E = dtype == 0 ? 8 : 4;
+    const int64_t chunks = static_cast<int64_t>(n_tok) * H * (D / E);
+    int blocks = static_cast<int>((chunks + 255) / 256);
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) blocks = 1;
+    if (dtype == 0) {
+        if (D == 64)
+            hipLaunchKernelGGL((rope_kernel<uint16_t, 64>), dim3(blocks), dim3(256), 0, stream,
+                               static_cast<uint16_t*>(q), static_cast<uint16_t*>(k), pos, rope, H, n_tok);
+        else
+            hipLaunchKernelGGL((rope_kernel<uint16_t, 32>), dim3(blocks), dim3(256), 0, stream,
+                               static_cast<uint16_t*>(q), static_cast<uint16_t*>(k), pos, rope, H, n_tok);
+    } else {
+        if (D == 64)
+            hipLaunchKernelGGL((rope_kernel<float, 64>), dim3(blocks), dim3(256), 0, stream,
+                               static_cast<float*>(q), static_cast<float*>(k), pos, rope, H, n_tok);
+        else
+            hipLaunchKernelGGL((rope_kernel<float, 32>), dim3(blocks), dim3(256), 0, stream,
+                               static_cast<float*>(q), static_cast<float*>(k), pos, rope, H, n_tok);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_builder(const BuilderArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(builder_kernel, dim3(1), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_mask(int F, int P, int W, int S, int token_level, uint8_t* out,
+                       hipStream_t stream) {
+    const int64_t n = token_level ? static_cast<int64_t>(F) * P : F;
+    int64_t blocks = (n * n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(mask_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, F, P, W,
+                       S, token_level, out);
+    return hipGetLastError();
+}
+
+}  // namespace swa

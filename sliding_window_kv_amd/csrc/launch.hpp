@@ -1,0 +1,59 @@
+// Host-side launchers of the gfx950 kernels (defined in the .hip files).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels_common.hpp"
+
+namespace swa {
+
+// 3-D RoPE band description (host-computed frequency ladder).
+struct RopeArgs {
+    int pairs_t, pairs_h, pairs_w;
+    double freq[64];         // per pair: theta^(-kk / d_band)
+};
+
+// Copy n_tok tokens of k, v ([n_tok, H, D]) into rows [row0, row0 + n_tok)
+// of the K region ([H][rows][D]) and the transposed V region ([H][D][rows]).
+// With rope != null, k is rotated on the way and q ([n_tok, H, D]) is
+// rotated in place.  meta_slot, if not null, receives frame_id.
+hipError_t launch_append(int dtype, int H, int D, int n_tok, int row0, int rows, const void* k,
+                         const void* v, void* kreg, void* vreg, void* q, const int32_t* pos,
+                         const RopeArgs* rope, int32_t* meta_slot, int32_t frame_id,
+                         hipStream_t stream);
+
+// Copy `ns` rows starting at src_row of every head (K and V^T) to dst_row;
+// meta_slot, if not null, receives frame_id.
+hipError_t launch_retain(int dtype, int H, int D, int rows, int src_row, int dst_row, int ns,
+                         void* kreg, void* vreg, int32_t* meta_slot, int32_t frame_id,
+                         hipStream_t stream);
+
+hipError_t launch_rope(int dtype, int n_tok, int H, int D, void* q, void* k, const int32_t* pos,
+                       const RopeArgs& rope, hipStream_t stream);
+
+struct BuilderArgs {
+    const int32_t* ord_frame;
+    const int32_t* pending_frame;
+    const int32_t* special_frame;
+    int32_t* out;            // records, 5 int32 each
+    int64_t n_key, n_special;
+    int n_win, pending;
+    int S, W, P, R, ns, cross, num_slots, n_ord;
+    int total;               // records to write
+};
+hipError_t launch_builder(const BuilderArgs& a, hipStream_t stream);
+
+hipError_t launch_mask(int F, int P, int W, int S, int token_level, uint8_t* out,
+                       hipStream_t stream);
+
+// Attention: bf16 on MFMA or fp32 on the vector ALUs; split > 1 writes
+// partials that launch_combine merges.
+hipError_t launch_attention(int dtype, int D, bool prefill, const AttnParams& p, int grid,
+                            hipStream_t stream);
+int attention_q_tile(int dtype);
+
+hipError_t launch_combine(int dtype, int D, int H, int nq, int splits, const float* part_o,
+                          const float* part_ml, void* out, float* lse, hipStream_t stream);
+
+}  // namespace swa

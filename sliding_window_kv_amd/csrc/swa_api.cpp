@@ -1,0 +1,549 @@
+// C ABI of the library (declared in include/swa.h): argument checks, the
+// cache's pool layout, host ring bookkeeping and kernel orchestration.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <type_traits>
+#include <vector>
+
+#include "launch.hpp"
+#include "ring.hpp"
+#include "swa.h"
+
+static_assert(std::is_same<swa_stream_t, hipStream_t>::value, "swa_stream_t must be hipStream_t");
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+    g_err = msg;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(SWA_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+struct Layout {
+    int P, H, D, elem, W, S, num_slots, n_ord, nspid, R, ns, rows, special_row_base;
+    int max_records;
+    int64_t k_bytes, v_bytes, meta_bytes, layer_bytes, work_offset, work_bytes;
+    int64_t meta_pending, meta_special, meta_records;   // int32 offsets inside meta
+    int64_t total_bytes;
+    int64_t part_o_floats;                               // floats of the O partials
+};
+
+int check_config(const swa_config* c, std::string* err) {
+    if (c == nullptr) return *err = "null config", SWA_E_INVAL;
+    if (c->num_layers < 1) return *err = "num_layers must be >= 1", SWA_E_INVAL;
+    if (c->tokens_per_frame < 1 || c->tokens_per_frame > (1 << 20))
+        return *err = "tokens_per_frame out of range", SWA_E_INVAL;
+    if (c->num_heads < 1 || c->num_heads > 1024) return *err = "num_heads out of range", SWA_E_INVAL;
+    if (c->head_dim != 32 && c->head_dim != 64) return *err = "head_dim must be 32 or 64", SWA_E_UNSUPPORTED;
+    if (c->dtype != SWA_BF16 && c->dtype != SWA_F32) return *err = "dtype must be SWA_BF16 or SWA_F32", SWA_E_INVAL;
+    if (c->sliding_window_size == 0 || c->sliding_window_size < -1)
+        return *err = "sliding_window_size must be -1 or positive", SWA_E_INVAL;
+    if (c->num_frame_per_block < 1) return *err = "num_frame_per_block must be >= 1", SWA_E_INVAL;
+    if (c->scale_frames < 0) return *err = "scale_frames must be >= 0", SWA_E_INVAL;
+    if (c->sliding_window_size == -1 && c->max_frames < 1)
+        return *err = "max_frames must be >= 1 when the window is off", SWA_E_INVAL;
+    if (c->cross_frame_special) {
+        if (c->special_rows < 1 || c->special_row0 < 0 ||
+            c->special_row0 + c->special_rows > c->tokens_per_frame)
+            return *err = "special rows must lie inside a frame", SWA_E_INVAL;
+        if (c->max_special_frames < 1) return *err = "max_special_frames must be >= 1", SWA_E_INVAL;
+    }
+    const int64_t W = c->sliding_window_size == -1
+                          ? -1
+                          : static_cast<int64_t>(c->sliding_window_size) * c->num_frame_per_block;
+    const int64_t slots = W >= 0 ? c->scale_frames + W + 1 : c->max_frames + 1;
+    const int64_t sp = c->cross_frame_special ? static_cast<int64_t>(c->max_special_frames) * c->special_rows : 0;
+    if (slots * c->tokens_per_frame + sp + 128 > (1ll << 30) || W > (1 << 24))
+        return *err = "cache row space too large", SWA_E_INVAL;
+    const int pairs = c->rope_pairs_t + c->rope_pairs_h + c->rope_pairs_w;
+    if (pairs != 0 && (pairs != c->head_dim / 2 || c->rope_pairs_t < 0 || c->rope_pairs_h < 0 ||
+                       c->rope_pairs_w < 0 || !(c->rope_theta > 0.f)))
+        return *err = "rope bands must add up to head_dim/2 with theta > 0", SWA_E_INVAL;
+    return SWA_OK;
+}
+
+Layout make_layout(const swa_config* c) {
+    Layout L{};
+    L.P = c->tokens_per_frame;
+    L.H = c->num_heads;
+    L.D = c->head_dim;
+    L.elem = c->dtype == SWA_BF16 ? 2 : 4;
+    L.W = c->sliding_window_size == -1 ? -1 : c->sliding_window_size * c->num_frame_per_block;
+    L.S = c->scale_frames;
+    L.num_slots = L.W >= 0 ? L.S + L.W + 1 : c->max_frames + 1;
+    L.n_ord = L.W >= 0 ? L.S + L.W + 1 : c->max_frames;
+    L.R = c->cross_frame_special ? c->max_special_frames : 0;
+    L.ns = c->cross_frame_special ? c->special_rows : 0;
+    L.nspid = c->cross_frame_special ? L.R + 1 : 1;
+    L.special_row_base = L.num_slots * L.P;
+    L.rows = static_cast<int>(align_up(static_cast<int64_t>(L.special_row_base) + int64_t(L.R) * L.ns + 64, 64));
+    L.max_records = L.num_slots + L.R;
+    L.k_bytes = align_up(int64_t(L.H) * L.rows * L.D * L.elem, 256);
+    L.v_bytes = L.k_bytes;
+    L.meta_pending = L.n_ord;
+    L.meta_special = L.n_ord + 1;
+    L.meta_records = align_up(L.meta_special + L.nspid, 4);
+    L.meta_bytes = align_up((L.meta_records + int64_t(L.max_records) * 5) * 4, 256);
+    L.layer_bytes = L.k_bytes + L.v_bytes + L.meta_bytes;
+    L.work_offset = L.layer_bytes * c->num_layers;
+    if (c->dtype == SWA_BF16) {
+        L.part_o_floats = int64_t(swa::kMaxSplits) * L.H * L.P * L.D;
+        L.work_bytes = align_up(L.part_o_floats * 4, 256) + align_up(int64_t(swa::kMaxSplits) * L.H * L.P * 2 * 4, 256);
+    } else {
+        L.part_o_floats = 0;
+        L.work_bytes = 0;
+    }
+    L.total_bytes = L.work_offset + L.work_bytes;
+    return L;
+}
+
+swa::RingConfig ring_config(const swa_config* c, const Layout& L) {
+    swa::RingConfig r;
+    r.P = L.P;
+    r.S = L.S;
+    r.W = L.W;
+    r.max_frames = c->max_frames;
+    r.cross_special = c->cross_frame_special != 0;
+    r.special_row0 = c->special_row0;
+    r.ns = L.ns;
+    r.R = L.R;
+    return r;
+}
+
+void make_rope(int pt, int ph, int pw, float theta, swa::RopeArgs* r) {
+    std::memset(r, 0, sizeof(*r));
+    r->pairs_t = pt;
+    r->pairs_h = ph;
+    r->pairs_w = pw;
+    const int bands[3] = {pt, ph, pw};
+    int p = 0;
+    for (int b = 0; b < 3; ++b)
+        for (int kk = 0; kk < bands[b]; ++kk)
+            r->freq[p++] = std::pow(static_cast<double>(theta), -static_cast<double>(kk) / bands[b]);
+}
+
+int tiles_of(int lo, int hi) { return (hi - (lo & ~7) + 63) / 64; }
+
+}  // namespace
+
+struct swa_cache {
+    swa_config cfg;
+    Layout L;
+    char* pool = nullptr;
+    bool dry = false;
+    int splits = 0;          // 0 = automatic
+    int num_cus = 256;
+    std::vector<swa::Ring> rings;
+    swa::RopeArgs rope;
+
+    char* layer_base(int l) const { return pool + int64_t(l) * L.layer_bytes; }
+    void* kreg(int l) const { return layer_base(l); }
+    void* vreg(int l) const { return layer_base(l) + L.k_bytes; }
+    int32_t* meta(int l) const { return reinterpret_cast<int32_t*>(layer_base(l) + L.k_bytes + L.v_bytes); }
+    float* part_o() const { return reinterpret_cast<float*>(pool + L.work_offset); }
+    float* part_ml() const {
+        return reinterpret_cast<float*>(pool + L.work_offset + align_up(L.part_o_floats * 4, 256));
+    }
+};
+
+namespace {
+
+int check_layer(const swa_cache* c, int layer) {
+    if (c == nullptr) return fail(SWA_E_INVAL, "null cache");
+    if (layer < 0 || layer >= c->cfg.num_layers) return fail(SWA_E_INVAL, "layer index out of range");
+    return SWA_OK;
+}
+
+int pick_splits(const swa_cache* c, int groups, int total_tiles) {
+    int s = c->splits;
+    if (s <= 0) {
+        const int target = 4 * c->num_cus;
+        s = (target + groups - 1) / groups;
+    }
+    s = std::min(s, swa::kMaxSplits);
+    s = std::min(s, std::max(1, total_tiles / 2));
+    return std::max(s, 1);
+}
+
+// Enqueue the device side of one append (special-row retention first, then
+// the frame copy with optional RoPE).
+int enqueue_append(swa_cache* c, int layer, const swa::AppendPlan& plan, int64_t t, void* q,
+                   const void* k, const void* v, const int32_t* pos, hipStream_t stream) {
+    const Layout& L = c->L;
+    const int dt = c->cfg.dtype;
+    if (plan.retain) {
+        const int src = plan.victim_slot * L.P + c->cfg.special_row0;
+        const int dst = L.special_row_base + plan.special_slot * L.ns;
+        hipError_t e = swa::launch_retain(dt, L.H, L.D, L.rows, src, dst, L.ns, c->kreg(layer), c->vreg(layer),
+                                          c->meta(layer) + L.meta_special + plan.special_id_index,
+                                          static_cast<int32_t>(plan.victim_frame), stream);
+        if (e != hipSuccess) return hip_fail(e, "retain kernel launch");
+    }
+    int32_t* slot_meta = plan.keyframe ? c->meta(layer) + plan.ord_index : c->meta(layer) + L.meta_pending;
+    hipError_t e = swa::launch_append(dt, L.H, L.D, L.P, plan.slot * L.P, L.rows, k, v, c->kreg(layer),
+                                      c->vreg(layer), q, pos, pos != nullptr ? &c->rope : nullptr, slot_meta,
+                                      static_cast<int32_t>(t), stream);
+    if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+    return SWA_OK;
+}
+
+// Attention of q over the layer's visible rows (split-KV + combine for bf16).
+int enqueue_attention(swa_cache* c, int layer, const void* q, void* out, float* lse, hipStream_t stream) {
+    const swa::Ring& ring = c->rings[layer];
+    const Layout& L = c->L;
+    std::vector<swa::RowSeg> segs;
+    ring.segments(&segs);
+    swa::AttnParams p{};
+    p.q = q;
+    p.kreg = c->kreg(layer);
+    p.vreg = c->vreg(layer);
+    p.out = out;
+    p.lse = lse;
+    p.nq = L.P;
+    p.H = L.H;
+    p.rows = L.rows;
+    p.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(L.D)));
+    p.F = 1;
+    p.seg.n = static_cast<int>(segs.size());
+    int tiles = 0;
+    for (int i = 0; i < swa::kMaxSegs; ++i) {
+        if (i < p.seg.n) {
+            p.seg.lo[i] = segs[i].lo;
+            p.seg.hi[i] = segs[i].hi;
+            p.seg.tile0[i] = tiles;
+            tiles += tiles_of(segs[i].lo, segs[i].hi);
+        } else {
+            p.seg.lo[i] = p.seg.hi[i] = 0;
+            p.seg.tile0[i] = 1 << 30;
+        }
+    }
+    p.seg.total_tiles = tiles;
+    if (p.seg.n > swa::kMaxSegs) return fail(SWA_E_STATE, "internal: bad segment list");
+    if (p.seg.n == 0) return fail(SWA_E_STATE, "no cached frame to attend to");
+    const int qrows = swa::attention_q_tile(c->cfg.dtype);
+    p.qtiles = (L.P + qrows - 1) / qrows;
+    int splits = 1;
+    if (c->cfg.dtype == SWA_BF16) splits = pick_splits(c, L.H * p.qtiles, tiles);
+    p.splits = splits;
+    p.part_o = c->part_o();
+    p.part_ml = c->part_ml();
+    hipError_t e = swa::launch_attention(c->cfg.dtype, L.D, false, p, L.H * splits * p.qtiles, stream);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    if (splits > 1) {
+        e = swa::launch_combine(c->cfg.dtype, L.D, L.H, L.P, splits, p.part_o, p.part_ml, out, lse, stream);
+        if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+    }
+    return SWA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t swa_cache_pool_bytes(const swa_config* cfg) {
+    std::string err;
+    if (check_config(cfg, &err) != SWA_OK) {
+        g_err = err;
+        return 0;
+    }
+    return static_cast<size_t>(make_layout(cfg).total_bytes);
+}
+
+int swa_cache_create(const swa_config* cfg, void* dev_pool, size_t pool_bytes, swa_cache** out) {
+    if (out == nullptr) return fail(SWA_E_INVAL, "null output handle");
+    *out = nullptr;
+    std::string err;
+    const int rc = check_config(cfg, &err);
+    if (rc != SWA_OK) return fail(rc, err);
+    const Layout L = make_layout(cfg);
+    const bool dry = dev_pool == nullptr && pool_bytes == 0;
+    if (!dry) {
+        if (dev_pool == nullptr) return fail(SWA_E_INVAL, "null pool with nonzero size");
+        if (reinterpret_cast<uintptr_t>(dev_pool) % 256 != 0) return fail(SWA_E_INVAL, "pool must be 256-byte aligned");
+        if (pool_bytes < static_cast<size_t>(L.total_bytes))
+            return fail(SWA_E_INVAL, "pool smaller than swa_cache_pool_bytes()");
+    }
+    swa_cache* c = new (std::nothrow) swa_cache();
+    if (c == nullptr) return fail(SWA_E_INVAL, "out of host memory");
+    c->cfg = *cfg;
+    c->L = L;
+    c->pool = static_cast<char*>(dev_pool);
+    c->dry = dry;
+    const swa::RingConfig rc2 = ring_config(cfg, L);
+    c->rings.reserve(cfg->num_layers);
+    for (int i = 0; i < cfg->num_layers; ++i) c->rings.emplace_back(rc2);
+    make_rope(cfg->rope_pairs_t, cfg->rope_pairs_h, cfg->rope_pairs_w, cfg->rope_theta, &c->rope);
+    if (!dry) {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+            prop.multiProcessorCount > 0)
+            c->num_cus = prop.multiProcessorCount;
+    }
+    *out = c;
+    return SWA_OK;
+}
+
+int swa_cache_destroy(swa_cache* cache) {
+    delete cache;
+    return SWA_OK;
+}
+
+int swa_cache_layout(const swa_cache* c, swa_layout* out) {
+    if (c == nullptr || out == nullptr) return fail(SWA_E_INVAL, "null argument");
+    const Layout& L = c->L;
+    out->layer_bytes = L.layer_bytes;
+    out->k_offset = 0;
+    out->v_offset = L.k_bytes;
+    out->meta_offset = L.k_bytes + L.v_bytes;
+    out->work_offset = L.work_offset;
+    out->work_bytes = L.work_bytes;
+    out->rows = L.rows;
+    out->num_slots = L.num_slots;
+    out->special_row_base = L.special_row_base;
+    out->elem_bytes = L.elem;
+    out->window_frames = L.W;
+    out->scratch_slot = L.num_slots - 1;
+    return SWA_OK;
+}
+
+int swa_cache_set_splits(swa_cache* c, int splits) {
+    if (c == nullptr) return fail(SWA_E_INVAL, "null cache");
+    if (splits < 0 || splits > swa::kMaxSplits) return fail(SWA_E_INVAL, "splits must be 0..32");
+    c->splits = splits;
+    return SWA_OK;
+}
+
+int kvcache_reset(swa_cache* c, swa_stream_t) {
+    if (c == nullptr) return fail(SWA_E_INVAL, "null cache");
+    for (auto& r : c->rings) r.reset();
+    return SWA_OK;
+}
+
+int kvcache_append(swa_cache* c, int layer, int64_t t, const void* k, const void* v, int keyframe,
+                   swa_stream_t stream) {
+    int rc = check_layer(c, layer);
+    if (rc != SWA_OK) return rc;
+    if (!c->dry && (k == nullptr || v == nullptr)) return fail(SWA_E_INVAL, "null k or v");
+    swa::AppendPlan plan;
+    std::string err;
+    rc = c->rings[layer].plan_append(t, keyframe != 0, &plan, &err);
+    if (rc != SWA_OK) return fail(rc, err);
+    if (!c->dry) {
+        rc = enqueue_append(c, layer, plan, t, nullptr, k, v, nullptr, stream);
+        if (rc != SWA_OK) return rc;
+    }
+    c->rings[layer].commit_append(plan, t);
+    return SWA_OK;
+}
+
+int kvcache_evict(swa_cache* c, int layer, swa_stream_t) {
+    const int rc = check_layer(c, layer);
+    if (rc != SWA_OK) return rc;
+    c->rings[layer].evict();
+    return SWA_OK;
+}
+
+int kvcache_rollback(swa_cache* c, int layer, swa_stream_t) {
+    int rc = check_layer(c, layer);
+    if (rc != SWA_OK) return rc;
+    std::string err;
+    rc = c->rings[layer].rollback(&err);
+    if (rc != SWA_OK) return fail(rc, err);
+    return SWA_OK;
+}
+
+int kvcache_attend(swa_cache* c, int layer, const void* q, void* out, float* lse, swa_stream_t stream) {
+    const int rc = check_layer(c, layer);
+    if (rc != SWA_OK) return rc;
+    if (c->dry) return fail(SWA_E_STATE, "bookkeeping-only cache cannot attend");
+    if (q == nullptr || out == nullptr) return fail(SWA_E_INVAL, "null tensor");
+    return enqueue_attention(c, layer, q, out, lse, stream);
+}
+
+int kvcache_visible_pages(const swa_cache* c, int layer, swa_page* out, int cap, int* n_out) {
+    const int rc = check_layer(c, layer);
+    if (rc != SWA_OK) return rc;
+    if (n_out == nullptr || cap < 0 || (cap > 0 && out == nullptr)) return fail(SWA_E_INVAL, "bad output buffer");
+    std::vector<swa::PageRec> recs;
+    c->rings[layer].pages(&recs);
+    *n_out = static_cast<int>(recs.size());
+    const int n = std::min<int>(cap, static_cast<int>(recs.size()));
+    for (int i = 0; i < n; ++i) {
+        out[i].frame = recs[i].frame;
+        out[i].region = recs[i].region;
+        out[i].slot = recs[i].slot;
+        out[i].row0 = recs[i].row0;
+        out[i].nrows = recs[i].nrows;
+    }
+    return SWA_OK;
+}
+
+int kvcache_read_device_pages(swa_cache* c, int layer, swa_page* host_out, int cap, int* n_out,
+                              swa_stream_t stream) {
+    int rc = check_layer(c, layer);
+    if (rc != SWA_OK) return rc;
+    if (c->dry) return fail(SWA_E_STATE, "bookkeeping-only cache has no device state");
+    if (n_out == nullptr || cap < 0 || (cap > 0 && host_out == nullptr)) return fail(SWA_E_INVAL, "bad output buffer");
+    const swa::Ring& ring = c->rings[layer];
+    const swa::RingCounters cnt = ring.counters();
+    std::vector<swa::PageRec> recs;
+    ring.pages(&recs);
+    const int total = static_cast<int>(recs.size());
+    *n_out = total;
+    if (total == 0) return SWA_OK;
+    const Layout& L = c->L;
+    int32_t* meta = c->meta(layer);
+    swa::BuilderArgs a{};
+    a.ord_frame = meta;
+    a.pending_frame = meta + L.meta_pending;
+    a.special_frame = meta + L.meta_special;
+    a.out = meta + L.meta_records;
+    a.n_key = cnt.n_key;
+    a.n_special = cnt.n_special;
+    a.n_win = cnt.n_win;
+    a.pending = cnt.pending;
+    a.S = L.S;
+    a.W = L.W;
+    a.P = L.P;
+    a.R = L.R;
+    a.ns = L.ns;
+    a.cross = c->cfg.cross_frame_special ? 1 : 0;
+    a.num_slots = L.num_slots;
+    a.n_ord = L.n_ord;
+    a.total = total;
+    hipError_t e = swa::launch_builder(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "page-list builder launch");
+    std::vector<int32_t> buf(size_t(total) * 5);
+    e = hipMemcpyAsync(buf.data(), a.out, buf.size() * 4, hipMemcpyDeviceToHost, stream);
+    if (e != hipSuccess) return hip_fail(e, "page-list copy");
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+    const int n = std::min(cap, total);
+    for (int i = 0; i < n; ++i) {
+        host_out[i].frame = buf[5 * i];
+        host_out[i].region = buf[5 * i + 1];
+        host_out[i].slot = buf[5 * i + 2];
+        host_out[i].row0 = buf[5 * i + 3];
+        host_out[i].nrows = buf[5 * i + 4];
+    }
+    return SWA_OK;
+}
+
+int rope3d_apply(void* q, void* k, const int32_t* pos, int n_tokens, int H, int D, int pt, int ph, int pw,
+                 float theta, int dtype, swa_stream_t stream) {
+    if (pos == nullptr || (q == nullptr && k == nullptr)) return fail(SWA_E_INVAL, "null pointer");
+    if (n_tokens < 0 || H < 1) return fail(SWA_E_INVAL, "bad shape");
+    if (D != 32 && D != 64) return fail(SWA_E_UNSUPPORTED, "head_dim must be 32 or 64");
+    if (dtype != SWA_BF16 && dtype != SWA_F32) return fail(SWA_E_INVAL, "bad dtype");
+    if (pt < 0 || ph < 0 || pw < 0 || pt + ph + pw != D / 2 || !(theta > 0.f))
+        return fail(SWA_E_INVAL, "rope bands must add up to head_dim/2 with theta > 0");
+    if (n_tokens == 0) return SWA_OK;
+    swa::RopeArgs r;
+    make_rope(pt, ph, pw, theta, &r);
+    hipError_t e = swa::launch_rope(dtype, n_tokens, H, D, q, k, pos, r, stream);
+    if (e != hipSuccess) return hip_fail(e, "rope kernel launch");
+    return SWA_OK;
+}
+
+int swa_stream_step(swa_cache* c, int layer, int64_t t, void* q, const void* k, const void* v,
+                    const int32_t* pos, int keyframe, void* out, float* lse, swa_stream_t stream) {
+    int rc = check_layer(c, layer);
+    if (rc != SWA_OK) return rc;
+    if (c->dry) return fail(SWA_E_STATE, "bookkeeping-only cache cannot attend");
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return fail(SWA_E_INVAL, "null tensor");
+    if (pos != nullptr && c->cfg.rope_pairs_t + c->cfg.rope_pairs_h + c->cfg.rope_pairs_w == 0)
+        return fail(SWA_E_INVAL, "positions given but the config has no rope bands");
+    swa::Ring& ring = c->rings[layer];
+    swa::AppendPlan plan;
+    std::string err;
+    rc = ring.plan_append(t, keyframe != 0, &plan, &err);
+    if (rc != SWA_OK) return fail(rc, err);
+    rc = enqueue_append(c, layer, plan, t, q, k, v, pos, stream);
+    if (rc != SWA_OK) return rc;
+    ring.commit_append(plan, t);
+    if (keyframe) ring.evict();
+
+    rc = enqueue_attention(c, layer, q, out, lse, stream);
+    if (rc != SWA_OK) return rc;
+    if (!keyframe) {
+        rc = ring.rollback(&err);
+        if (rc != SWA_OK) return fail(rc, err);
+    }
+    return SWA_OK;
+}
+
+size_t swa_prefill_workspace_bytes(int F, int P, int H, int D, int dtype) {
+    if (F < 1 || P < 1 || H < 1 || (D != 32 && D != 64) || (dtype != SWA_BF16 && dtype != SWA_F32)) return 0;
+    const int64_t rows = align_up(int64_t(F) * P + 64, 64);
+    const int64_t elem = dtype == SWA_BF16 ? 2 : 4;
+    return static_cast<size_t>(2 * align_up(int64_t(H) * rows * D * elem, 256));
+}
+
+int swa_prefill_masked(const void* q, const void* k, const void* v, int F, int P, int H, int D, int sws,
+                       int nfpb, int S, int dtype, void* out, float* lse, void* ws, size_t ws_bytes,
+                       swa_stream_t stream) {
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return fail(SWA_E_INVAL, "null tensor");
+    if (F < 1 || P < 1 || H < 1) return fail(SWA_E_INVAL, "F, P and H must be >= 1");
+    if (int64_t(F) * P + 128 > (1ll << 30)) return fail(SWA_E_INVAL, "too many tokens");
+    if (D != 32 && D != 64) return fail(SWA_E_UNSUPPORTED, "head_dim must be 32 or 64");
+    if (dtype != SWA_BF16 && dtype != SWA_F32) return fail(SWA_E_INVAL, "bad dtype");
+    if (sws == 0 || sws < -1 || nfpb < 1 || S < 0) return fail(SWA_E_INVAL, "bad window arguments");
+    const size_t need = swa_prefill_workspace_bytes(F, P, H, D, dtype);
+    if (ws == nullptr || ws_bytes < need) return fail(SWA_E_INVAL, "workspace smaller than swa_prefill_workspace_bytes()");
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(SWA_E_INVAL, "workspace must be 256-byte aligned");
+    const int W = sws == -1 ? -1 : sws * nfpb;
+    const int rows = static_cast<int>(align_up(int64_t(F) * P + 64, 64));
+    void* kreg = ws;
+    void* vreg = static_cast<char*>(ws) + need / 2;
+    // the F frames laid out as consecutive pages (frame f in rows [f*P, (f+1)*P))
+    hipError_t e = swa::launch_append(dtype, H, D, F * P, 0, rows, k, v, kreg, vreg, nullptr, nullptr, nullptr,
+                                      nullptr, 0, stream);
+    if (e != hipSuccess) return hip_fail(e, "chunk layout kernel launch");
+    swa::AttnParams p{};
+    p.q = q;
+    p.kreg = kreg;
+    p.vreg = vreg;
+    p.out = out;
+    p.lse = lse;
+    p.nq = P;
+    p.H = H;
+    p.rows = rows;
+    p.splits = 1;
+    p.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
+    p.F = F;
+    p.W = W;
+    p.S = S;
+    p.fP = P;
+    const int qrows = swa::attention_q_tile(dtype);
+    p.qtiles = (P + qrows - 1) / qrows;
+    e = swa::launch_attention(dtype, D, true, p, F * H * p.qtiles, stream);
+    if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+    return SWA_OK;
+}
+
+int swa_prefill_mask(int F, int P, int sws, int nfpb, int S, int token_level, uint8_t* dev_out,
+                     swa_stream_t stream) {
+    if (dev_out == nullptr) return fail(SWA_E_INVAL, "null output");
+    if (F < 1 || P < 1 || sws == 0 || sws < -1 || nfpb < 1 || S < 0) return fail(SWA_E_INVAL, "bad arguments");
+    const int W = sws == -1 ? -1 : sws * nfpb;
+    hipError_t e = swa::launch_mask(F, P, W, S, token_level ? 1 : 0, dev_out, stream);
+    if (e != hipSuccess) return hip_fail(e, "mask kernel launch");
+    return SWA_OK;
+}
+
+const char* swa_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,188 @@
+"""C-ABI checks that need no GPU: exported symbols, argument validation and
+the host ring bookkeeping (page lists bit-exact against the oracle's naive
+ring cache).  Only bookkeeping-only caches are used here; no kernel runs."""
+import ctypes
+
+import numpy as np
+import pytest
+from hypothesis import given, strategies as st
+
+import sliding_window_kv_amd as swa
+from oracle import CacheConfig, NaiveRingCache, RingError
+
+
+def test_library_exports_every_header_function():
+    L = swa.lib()
+    names = swa.header_functions()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in swa._PROTOS, n
+
+
+def test_pool_bytes_and_layout():
+    c = swa.make_config(1374, 16, 64, sliding_window_size=16, scale_frames=8)
+    nb = swa.swa_cache_pool_bytes(c)
+    h = swa.swa_cache_create(c, None, 0)
+    L = swa.swa_cache_layout(h)
+    assert L.num_slots == 8 + 16 + 1 and L.scratch_slot == 24
+    assert L.window_frames == 16 and L.elem_bytes == 2
+    assert L.rows % 64 == 0 and L.rows >= 25 * 1374 + 64
+    assert L.v_offset == L.k_offset + 16 * L.rows * 64 * 2
+    assert nb == L.work_offset + L.work_bytes
+    swa.swa_cache_destroy(h)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("sliding_window_size", 0, swa.SWA_E_INVAL),
+    ("sliding_window_size", -3, swa.SWA_E_INVAL),
+    ("head_dim", 48, swa.SWA_E_UNSUPPORTED),
+    ("num_frame_per_block", 0, swa.SWA_E_INVAL),
+    ("tokens_per_frame", 0, swa.SWA_E_INVAL),
+    ("dtype", 7, swa.SWA_E_INVAL),
+    ("scale_frames", -1, swa.SWA_E_INVAL),
+])
+def test_invalid_configs(field, value, code):
+    c = swa.make_config(21, 2, 32, sliding_window_size=2, scale_frames=1)
+    setattr(c, field, value)
+    assert swa.swa_cache_pool_bytes(c) == 0
+    with pytest.raises(swa.SwaError) as e:
+        swa.swa_cache_create(c, None, 0)
+    assert e.value.code == code
+    assert swa.swa_last_error() != ""
+
+
+def test_special_rows_must_fit_and_rope_bands_must_sum():
+    c = swa.make_config(4, 2, 32, sliding_window_size=2, cross_frame_special=True, special_rows=5)
+    with pytest.raises(swa.SwaError):
+        swa.swa_cache_create(c, None, 0)
+    c = swa.make_config(21, 2, 32, sliding_window_size=2, rope=(5, 5, 5))
+    with pytest.raises(swa.SwaError):
+        swa.swa_cache_create(c, None, 0)
+
+
+def test_bookkeeping_cache_refuses_device_work():
+    c = swa.make_config(21, 2, 32, sliding_window_size=2, scale_frames=1)
+    h = swa.swa_cache_create(c, None, 0)
+    with pytest.raises(swa.SwaError) as e:
+        swa.swa_stream_step(h, 0, 0, ctypes.c_void_p(8), ctypes.c_void_p(8), ctypes.c_void_p(8), None, 1,
+                            ctypes.c_void_p(8), None)
+    assert e.value.code == swa.SWA_E_STATE
+    with pytest.raises(swa.SwaError) as e:
+        swa.kvcache_read_device_pages(h, 0, 16)
+    assert e.value.code == swa.SWA_E_STATE
+    with pytest.raises(swa.SwaError) as e:
+        swa.kvcache_append(h, 5, 0, None, None, True)        # layer out of range
+    assert e.value.code == swa.SWA_E_INVAL
+
+
+def test_prefill_argument_checks():
+    need = swa.swa_prefill_workspace_bytes(4, 10, 2, 64, swa.SWA_BF16)
+    assert need > 0 and need % 256 == 0
+    assert swa.swa_prefill_workspace_bytes(4, 10, 2, 48, swa.SWA_BF16) == 0
+    p = ctypes.c_void_p(256)
+    with pytest.raises(swa.SwaError) as e:
+        swa.swa_prefill_masked(p, p, p, 4, 10, 2, 64, 0, 1, 0, swa.SWA_BF16, p, None, p, need)
+    assert e.value.code == swa.SWA_E_INVAL
+    with pytest.raises(swa.SwaError) as e:
+        swa.swa_prefill_masked(p, p, p, 4, 10, 2, 64, 2, 1, 0, swa.SWA_BF16, p, None, p, need - 1)
+    assert e.value.code == swa.SWA_E_INVAL
+    with pytest.raises(swa.SwaError) as e:
+        swa.rope3d_apply(p, p, p, 10, 2, 64, 10, 10, 10, 1e4, swa.SWA_BF16)
+    assert e.value.code == swa.SWA_E_INVAL
+
+
+def _pair(P, W, S, cross, ns, R, max_frames=50):
+    ocfg = CacheConfig(P=P, sliding_window_size=W, scale_frames=S, cross_frame_special=cross,
+                       special_row0=0, special_rows=ns, max_special_frames=R, max_frames=max_frames)
+    c = swa.make_config(P, 1, 32, sliding_window_size=W, scale_frames=S, cross_frame_special=cross,
+                        special_rows=ns, max_special_frames=R, max_frames=max_frames)
+    return NaiveRingCache(ocfg), swa.swa_cache_create(c, None, 0)
+
+
+def _kv(P):
+    z = np.zeros((P, 1, 1))
+    return z, z
+
+
+OPS = st.lists(st.sampled_from(["key", "key", "key", "nonkey", "evict", "rollback", "reset", "stale"]),
+               min_size=1, max_size=60)
+
+
+@given(P=st.integers(5, 9), W=st.sampled_from([-1, 1, 2, 3, 5]), S=st.integers(0, 3),
+       cross=st.booleans(), ns=st.integers(1, 3), R=st.integers(1, 4), ops=OPS)
+def test_page_lists_bit_exact_vs_oracle(P, W, S, cross, ns, R, ops):
+    ora, h = _pair(P, W, S, cross, ns, R, max_frames=12)
+    t = 0
+    try:
+        for op in ops:
+            expect_err = None
+            try:
+                if op == "key":
+                    ora.append(t, *_kv(P), True)
+                elif op == "nonkey":
+                    ora.append(t, *_kv(P), False)
+                elif op == "stale":
+                    ora.append(t - 2, *_kv(P), True)
+                elif op == "evict":
+                    ora.evict()
+                elif op == "rollback":
+                    ora.rollback()
+                else:
+                    ora.reset()
+            except RingError:
+                expect_err = True
+            got_err = None
+            try:
+                if op in ("key", "nonkey", "stale"):
+                    swa.kvcache_append(h, 0, t if op != "stale" else t - 2, None, None, op != "nonkey")
+                elif op == "evict":
+                    swa.kvcache_evict(h, 0)
+                elif op == "rollback":
+                    swa.kvcache_rollback(h, 0)
+                else:
+                    swa.kvcache_reset(h)
+            except swa.SwaError:
+                got_err = True
+            assert got_err == expect_err, op
+            if op in ("key", "nonkey"):
+                t += 1
+            if op == "reset":
+                t = 0
+            assert swa.kvcache_visible_pages(h, 0) == ora.visible_pages()
+    finally:
+        swa.swa_cache_destroy(h)
+
+
+def test_long_stream_with_specials_bit_exact():
+    # Ragged cross-frame-special workload shape: window 16, 8 scale frames,
+    # 5 special rows, every third frame a non-keyframe; R reduced to 40 so
+    # the special ring wraps several times within 400 frames.
+    ora, h = _pair(1405, 16, 8, True, 5, 40)
+    try:
+        for t in range(400):
+            kf = t % 3 != 2
+            ora.append(t, *_kv(1405), kf)
+            swa.kvcache_append(h, 0, t, None, None, kf)
+            if kf:
+                ora.evict()
+                swa.kvcache_evict(h, 0)
+            assert swa.kvcache_visible_pages(h, 0) == ora.visible_pages()
+            if not kf:
+                ora.rollback()
+                swa.kvcache_rollback(h, 0)
+    finally:
+        swa.swa_cache_destroy(h)
+
+
+def test_capacity_error_with_window_off():
+    ora, h = _pair(5, -1, 0, False, 1, 1, max_frames=3)
+    for t in range(3):
+        swa.kvcache_append(h, 0, t, None, None, True)
+    with pytest.raises(swa.SwaError) as e:
+        swa.kvcache_append(h, 0, 3, None, None, True)
+    assert e.value.code == swa.SWA_E_CAPACITY
+    # a non-keyframe still fits in the scratch slot
+    swa.kvcache_append(h, 0, 4, None, None, False)
+    assert swa.kvcache_visible_pages(h, 0)[-1] == (4, 0, 3, 0, 5)
+    swa.swa_cache_destroy(h)

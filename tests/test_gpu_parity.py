@@ -1,0 +1,311 @@
+"""GPU parity of the HIP path against the float64 oracle (MI355X only).
+
+Every call goes through the C ABI of libswa.so.  Tolerances: fp32 path
+max-abs 1e-5; bf16 path max-abs 2e-2 and mean-abs 2e-3 on N(0,1) inputs;
+page lists, masks and cache bytes bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sliding_window_kv_amd as swa
+from gpu_helpers import (assert_close_bf16, assert_close_f32, bf16_round_f64, case, dev, host)
+from oracle import (CacheConfig, NaiveRingCache, frame_visibility, masked_attention, prefill, rope3d,
+                    token_mask)
+from swa_synth import chunk_qkv, frame_positions, frame_qkv
+
+pytestmark = pytest.mark.gpu
+
+
+def _cache(P, H, D, dtype, W, S, nfpb=1, cross=False, ns=5, R=1000, max_frames=64, rope=(0, 0, 0),
+           num_layers=1):
+    cfg = swa.make_config(P, H, D, dtype=dtype, sliding_window_size=W, num_frame_per_block=nfpb,
+                          scale_frames=S, cross_frame_special=cross, special_rows=ns, max_special_frames=R,
+                          max_frames=max_frames, rope=rope, num_layers=num_layers)
+    ocfg = CacheConfig(P=P, sliding_window_size=W, num_frame_per_block=nfpb, scale_frames=S,
+                       cross_frame_special=cross, special_row0=0, special_rows=ns, max_special_frames=R,
+                       max_frames=max_frames)
+    return swa.SwaCache(cfg), NaiveRingCache(ocfg)
+
+
+# ---------------------------------------------------------------------------
+# tiny fp32 workload: 6 frames, P=21, H=2, D=32, window 2, 1 scale frame
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("W,S", [(2, 1), (-1, 0), (6, 0), (1, 0)])
+def test_prefill_f32_tiny(W, S):
+    F, P, H, D = 6, 21, 2, 32
+    case(f"prefill fp32 F={F} P={P} H={H} D={D} W={W} S={S}")
+    q, k, v = chunk_qkv(1, F, P, H, D, bf16=False)
+    ro, rl = prefill(q, k, v, F, P, W, 1, S)
+    out = torch.empty((F * P, H, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((H, F * P), dtype=torch.float32, device="cuda")
+    swa.prefill_t(dev(q, torch.float32), dev(k, torch.float32), dev(v, torch.float32), F, P, W, 1, S, out, lse)
+    assert_close_f32(host(out), ro, "out")
+    assert_close_f32(host(lse), rl, "lse")
+
+
+@pytest.mark.parametrize("W,S", [(2, 1), (-1, 0), (6, 0)])
+def test_stream_f32_tiny(W, S):
+    F, P, H, D = 6, 21, 2, 32
+    case(f"stream fp32 F={F} P={P} H={H} D={D} W={W} S={S}")
+    gc, oc = _cache(P, H, D, swa.SWA_F32, W, S, max_frames=8)
+    q, k, v = chunk_qkv(1, F, P, H, D, bf16=False)
+    po, pl = prefill(q, k, v, F, P, W, 1, S)
+    for t in range(F):
+        rows = slice(t * P, (t + 1) * P)
+        qd, kd, vd = (dev(x[rows], torch.float32) for x in (q, k, v))
+        out = torch.empty_like(qd)
+        lse = torch.empty((H, P), dtype=torch.float32, device="cuda")
+        gc.step(0, t, qd, kd, vd, True, out, lse)
+        ro, rl, pages = oc.step(t, q[rows], k[rows], v[rows], True)
+        assert_close_f32(host(out), ro, f"out t={t}")
+        assert_close_f32(host(lse), rl, f"lse t={t}")
+        # streaming step t equals row block t of the masked prefill
+        assert_close_f32(host(out), po[rows], f"stream==prefill t={t}")
+        assert gc.pages() == pages
+        dpages, n = gc.device_pages()
+        assert dpages == pages and n == len(pages)
+
+
+# ---------------------------------------------------------------------------
+# bf16 prefill over several tiles with ragged frames
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("F,P,H,D,W,nfpb,S", [
+    (5, 77, 2, 64, 2, 1, 1),
+    (7, 130, 3, 64, 2, 1, 2),
+    (4, 200, 2, 32, -1, 1, 0),
+    (6, 61, 2, 64, 1, 2, 1),
+])
+def test_prefill_bf16(F, P, H, D, W, nfpb, S):
+    case(f"prefill bf16 F={F} P={P} H={H} D={D} W={W} nfpb={nfpb} S={S}")
+    q, k, v = chunk_qkv(3, F, P, H, D)
+    ro, rl = prefill(q, k, v, F, P, W, nfpb, S)
+    out = torch.empty((F * P, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((H, F * P), dtype=torch.float32, device="cuda")
+    swa.prefill_t(dev(q), dev(k), dev(v), F, P, W, nfpb, S, out, lse)
+    assert_close_bf16(host(out), ro, "out")
+    assert np.abs(host(lse) - rl).max() <= 1e-2
+
+
+def test_prefill_mask_export_bit_exact():
+    for (F, P, W, nfpb, S) in [(10, 3, 4, 1, 0), (12, 2, 2, 3, 2), (7, 5, -1, 1, 0), (32, 1, 8, 1, 8)]:
+        case(f"mask F={F} P={P} W={W} nfpb={nfpb} S={S}")
+        fr = torch.empty((F, F), dtype=torch.uint8, device="cuda")
+        swa.prefill_mask_t(F, P, W, nfpb, S, False, fr)
+        assert np.array_equal(host(fr).astype(bool), frame_visibility(F, W, nfpb, S))
+        tok = torch.empty((F * P, F * P), dtype=torch.uint8, device="cuda")
+        swa.prefill_mask_t(F, P, W, nfpb, S, True, tok)
+        assert np.array_equal(host(tok).astype(bool), token_mask(F, P, W, nfpb, S))
+
+
+# ---------------------------------------------------------------------------
+# bf16 streaming with scale frames, retained specials and non-keyframes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("splits", [1, 3, 0])
+def test_stream_bf16_specials_nonkey(splits):
+    P, H, D, W, S, ns, R = 45, 2, 64, 3, 2, 5, 4
+    case(f"stream bf16 P={P} W={W} S={S} ns={ns} R={R} splits={splits}")
+    gc, oc = _cache(P, H, D, swa.SWA_BF16, W, S, cross=True, ns=ns, R=R)
+    gc.set_splits(splits)
+    for t in range(18):
+        kf = t % 3 != 2
+        q, k, v = frame_qkv(5, t, P, H, D)
+        qd, kd, vd = dev(q), dev(k), dev(v)
+        out = torch.empty_like(qd)
+        lse = torch.empty((H, P), dtype=torch.float32, device="cuda")
+        gc.step(0, t, qd, kd, vd, kf, out, lse)
+        ro, rl, pages = oc.step(t, q, k, v, kf)
+        assert_close_bf16(host(out), ro, f"out t={t}")
+        assert np.abs(host(lse) - rl).max() <= 1e-2
+        assert gc.pages() == oc.visible_pages()
+        if kf:
+            assert gc.device_pages()[0] == pages
+
+
+def test_cache_bytes_bit_exact():
+    # K rows and transposed V rows of every visible frame page and special
+    # entry equal the appended bf16 values exactly.
+    P, H, D, W, S, ns, R = 37, 2, 64, 2, 1, 3, 2
+    case(f"cache bytes P={P} W={W} S={S}")
+    gc, oc = _cache(P, H, D, swa.SWA_BF16, W, S, cross=True, ns=ns, R=R)
+    frames = {}
+    for t in range(9):
+        q, k, v = frame_qkv(6, t, P, H, D)
+        frames[t] = (k, v)
+        gc.append(0, t, dev(k), dev(v), True)
+        gc.evict(0)
+    torch.cuda.synchronize()
+    kr, vr = gc.region_views(0)
+    K = kr.float().cpu().numpy()
+    V = vr.float().cpu().numpy()
+    L = gc.layout
+    for (f, region, slot, row0, nrows) in gc.pages():
+        k, v = frames[f]
+        if region == swa.SWA_REGION_FRAME:
+            base = slot * P
+            assert np.array_equal(K[:, base:base + P, :], k.transpose(1, 0, 2))
+            assert np.array_equal(V[:, :, base:base + P], v.transpose(1, 2, 0))
+        else:
+            base = L.special_row_base + row0
+            assert np.array_equal(K[:, base:base + nrows, :], k[:nrows].transpose(1, 0, 2))
+            assert np.array_equal(V[:, :, base:base + nrows], v[:nrows].transpose(1, 2, 0))
+
+
+def test_frame_id_closed_form():
+    # q = 0 makes every visible key weigh the same: the output is the mean
+    # frame index of the visible rows, exact before the final bf16 rounding.
+    P, H, D, W, S, ns, R = 29, 2, 64, 3, 2, 5, 3
+    case("frame-id closed form")
+    gc, oc = _cache(P, H, D, swa.SWA_BF16, W, S, cross=True, ns=ns, R=R)
+    for t in range(14):
+        kf = t % 3 != 2
+        q = np.zeros((P, H, D), np.float32)
+        k = frame_qkv(7, t, P, H, D)[1]
+        v = np.full((P, H, D), float(t), np.float32)
+        qd, kd, vd = dev(q), dev(k), dev(v)
+        out = torch.empty_like(qd)
+        gc.step(0, t, qd, kd, vd, kf, out, None)
+        rows = [(f, nr) for (f, _, _, _, nr) in oc.step(t, q, k, v, kf)[2]]
+        mean = sum(f * nr for f, nr in rows) / sum(nr for _, nr in rows)
+        expect = bf16_round_f64(np.full((P, H, D), mean))
+        assert np.array_equal(host(out), expect), (t, mean)
+
+
+def test_nan_poisoned_pool():
+    # Every byte of the pool starts as NaN: rows outside the visible segments
+    # (page padding of the row space, unused slots, special ring) must never
+    # reach the output.
+    P, H, D, W, S = 50, 2, 64, 2, 1
+    case("NaN-poisoned pool")
+    gc, oc = _cache(P, H, D, swa.SWA_BF16, W, S, cross=True, ns=5, R=3)
+    gc.pool.fill_(255)          # 0xFFFF is a bf16 NaN
+    for t in range(10):
+        kf = t % 4 != 3
+        q, k, v = frame_qkv(8, t, P, H, D)
+        qd, kd, vd = dev(q), dev(k), dev(v)
+        out = torch.empty_like(qd)
+        gc.step(0, t, qd, kd, vd, kf, out, None)
+        ro, _, _ = oc.step(t, q, k, v, kf)
+        assert_close_bf16(host(out), ro, f"t={t}")
+
+
+def test_stream_equals_prefill_bf16():
+    F, P, H, D, W, S = 8, 96, 2, 64, 3, 2
+    case("stream == prefill bf16")
+    q, k, v = chunk_qkv(9, F, P, H, D)
+    pout = torch.empty((F * P, H, D), dtype=torch.bfloat16, device="cuda")
+    swa.prefill_t(dev(q), dev(k), dev(v), F, P, W, 1, S, pout, None)
+    gc, _ = _cache(P, H, D, swa.SWA_BF16, W, S)
+    gc.set_splits(1)
+    pg = host(pout)
+    for t in range(F):
+        rows = slice(t * P, (t + 1) * P)
+        qd, kd, vd = dev(q[rows]), dev(k[rows]), dev(v[rows])
+        out = torch.empty_like(qd)
+        gc.step(0, t, qd, kd, vd, True, out, None)
+        assert np.abs(host(out) - pg[rows]).max() <= 1e-2
+
+
+def test_multi_layer_caches_are_independent():
+    P, H, D = 33, 2, 64
+    case("two layers")
+    gc, _ = _cache(P, H, D, swa.SWA_BF16, 2, 1, num_layers=2)
+    oc = [NaiveRingCache(CacheConfig(P=P, sliding_window_size=2, scale_frames=1)) for _ in range(2)]
+    for t in range(6):
+        for layer in range(2):
+            q, k, v = frame_qkv(10 + layer, t, P, H, D)
+            qd, kd, vd = dev(q), dev(k), dev(v)
+            out = torch.empty_like(qd)
+            gc.step(layer, t, qd, kd, vd, True, out, None)
+            ro, _, _ = oc[layer].step(t, q, k, v, True)
+            assert_close_bf16(host(out), ro, f"layer {layer} t={t}")
+
+
+# ---------------------------------------------------------------------------
+# 3-D RoPE
+# ---------------------------------------------------------------------------
+
+def _ulp_bf16(x):
+    a = np.abs(x).astype(np.float32)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+@pytest.mark.parametrize("t", [0, 5, 1999])
+def test_rope3d_apply(t):
+    P, H, D = 1374, 4, 64
+    case(f"rope3d t={t}")
+    q, k, _ = frame_qkv(11, t, P, H, D)
+    pos = frame_positions(t, 37, 37, 5)
+    qd, kd = dev(q), dev(k)
+    swa.rope3d_t(qd, kd, torch.from_numpy(pos).cuda(), (12, 10, 10))
+    for got, x in ((host(qd), q), (host(kd), k)):
+        ref = rope3d(x, pos, 12, 10, 10)
+        diff = np.abs(got - bf16_round_f64(ref))
+        # one bf16 ulp of the exact value (floored at 2^-10 for values near 0,
+        # where single-precision cancellation dominates)
+        assert np.all(diff <= _ulp_bf16(np.maximum(np.abs(ref), 2.0 ** -10)) * 1.0001)
+
+
+def test_stream_with_rope_matches_oracle():
+    P, H, D, W, S = 1374, 2, 64, 4, 2
+    case("stream + fused rope")
+    gc, oc = _cache(P, H, D, swa.SWA_BF16, W, S, rope=(12, 10, 10))
+    for t in range(9):
+        q, k, v = frame_qkv(12, t, P, H, D)
+        pos = frame_positions(t, 37, 37, 5)
+        qd, kd, vd = dev(q), dev(k), dev(v)
+        out = torch.empty_like(qd)
+        gc.step(0, t, qd, kd, vd, True, out, None, pos=torch.from_numpy(pos).cuda())
+        qr = rope3d(q, pos, 12, 10, 10)
+        kr = rope3d(k, pos, 12, 10, 10)
+        ro, _, _ = oc.step(t, qr, kr, v, True)
+        assert_close_bf16(host(out), ro, f"t={t}")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled rows
+# ---------------------------------------------------------------------------
+
+SAMPLE_ROWS = np.array([0, 1, 4, 5, 63, 64, 127, 128, 700, 1279, 1280, 1300, 1343, 1344, 1373])
+
+
+def test_stream_step_full_size_sampled():
+    # Single streaming step workload: P=1374, H=16, D=64, 8 scale + 16 window
+    # frames (24 x 1374 = 32,976 visible keys), in the bench's launch config.
+    P, H, D, W, S = 1374, 16, 64, 16, 8
+    case("full-size stream step, sampled rows")
+    gc, oc = _cache(P, H, D, swa.SWA_BF16, W, S)
+    for t in range(30):
+        q, k, v = frame_qkv(2, t % 97, P, H, D)
+        qd, kd, vd = dev(q), dev(k), dev(v)
+        out = torch.empty_like(qd)
+        lse = torch.empty((H, P), dtype=torch.float32, device="cuda")
+        gc.step(0, t, qd, kd, vd, True, out, lse)
+        oc.append(t, k, v, True)
+        oc.evict()
+        if t in (0, 9, 29):
+            assert sum(p[4] for p in oc.visible_pages()) == min(t + 1, 24) * P
+            ro, rl = oc.attend(q[SAMPLE_ROWS])
+            assert_close_bf16(host(out)[SAMPLE_ROWS], ro, f"t={t}")
+            assert np.abs(host(lse)[:, SAMPLE_ROWS] - rl).max() <= 1e-2
+
+
+def test_prefill_full_size_sampled():
+    # Chunked prefill workload: 32 frames x 1374, window 8, 8 scale frames.
+    F, P, H, D, W, S = 32, 1374, 16, 64, 8, 8
+    case("full-size prefill, sampled rows")
+    q, k, v = chunk_qkv(3, F, P, H, D)
+    out = torch.empty((F * P, H, D), dtype=torch.bfloat16, device="cuda")
+    swa.prefill_t(dev(q), dev(k), dev(v), F, P, W, 1, S, out, None)
+    got = host(out)
+    vis = frame_visibility(F, W, 1, S)
+    fk = np.arange(F * P) // P
+    for i in (0, 7, 8, 15, 16, 31):
+        rows = i * P + SAMPLE_ROWS
+        mask = np.broadcast_to(vis[i][fk][None, :], (len(rows), F * P))
+        ro, _ = masked_attention(q[rows], k, v, mask)
+        assert_close_bf16(got[rows], ro, f"frame {i}")
