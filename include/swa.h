@@ -122,7 +122,10 @@ typedef struct swa_page {
  * Where the cache keeps its rows inside the caller's pool (bytes from the
  * pool base).  Per layer l, with E = element size:
  *   K   at k_offset + l*layer_bytes, laid out [H][rows][D]
- *   V^T at v_offset + l*layer_bytes, laid out [H][D][rows]
+ *   V^T at v_offset + l*layer_bytes, laid out [H][D][rows], where key r is
+ *       stored at position r with bits 2 and 3 swapped (a permutation inside
+ *       every aligned group of 16 keys; it matches the key order of one MFMA
+ *       lane's operand).
  * Page slot s holds a frame in rows [s*P, (s+1)*P); special-ring entry e
  * holds its rows at special_row_base + e*special_rows.
  */

@@ -16,6 +16,15 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kMaxSegs = 8;      // row segments per streaming attention call
 constexpr int kMaxSplits = 32;   // KV splits of one streaming attention call
 
+// Storage position of a key inside the transposed V region: within every
+// aligned group of 16 keys, bits 2 and 3 of the key index are swapped, so
+// that the 8 keys one MFMA lane supplies to O^T = V^T P^T (keys 4h..4h+3
+// and 8+4h..8+4h+3 of a 16-key step, h = lane half) are 8 consecutive
+// elements.  The map is its own inverse.
+__host__ __device__ __forceinline__ int vt_pos(int key) {
+    return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
 __device__ __forceinline__ float bf2f(uint16_t b) {
     return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
 }
@@ -25,8 +34,11 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Two floats to packed bf16 (lo in bits 0..15), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-    return static_cast<uint32_t>(f2bf(lo)) | (static_cast<uint32_t>(f2bf(hi)) << 16);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2v));
 }
 
 // Visible key frames of query frame i in a masked prefill (guide, "Mask

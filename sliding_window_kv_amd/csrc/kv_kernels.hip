@@ -4,8 +4,10 @@
 //
 // Cache layout of one layer (rows = the layer's row space):
 //   K   [H][rows][D]  -- a key row is D contiguous elements
-//   V^T [H][D][rows]  -- transposed, so the attention kernel reads 8
-//                        consecutive keys of one feature as one 16-byte load
+//   V^T [H][D][rows]  -- transposed, keys stored at vt_pos(key) (bits 2 and 3
+//                        swapped inside each 16-key group), so the attention
+//                        kernel reads the 8 keys one MFMA lane needs as one
+//                        16-byte load
 // A frame in page slot s owns rows [s*P, (s+1)*P) (guide "KV Cache Eviction
 // Strategy": whole frames enter and leave the cache).
 #include "launch.hpp"
@@ -64,7 +66,7 @@ __device__ __forceinline__ void rope_chunk(T* x, const RopeArgs& r, const int32_
 
 constexpr int kTileRows = 64;
 
-// One block = 64 destination rows (8-aligned) of one head.
+// One block = 64 destination rows (16-aligned) of one head.
 template <typename T, int D, bool ROPE>
 __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                      T* __restrict__ kreg, T* __restrict__ vreg,
@@ -77,7 +79,7 @@ __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, co
     __shared__ T vt[kTileRows * LD];
 
     const int h = blockIdx.y;
-    const int base = (row0 & ~7) + blockIdx.x * kTileRows;   // first destination row
+    const int base = (row0 & ~15) + blockIdx.x * kTileRows;  // first destination row
     const int tid = threadIdx.x;
 
     if (meta_slot != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *meta_slot = frame_id;
@@ -109,23 +111,31 @@ __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, co
     }
     __syncthreads();
 
-    // Transposed V: E consecutive rows of one feature per 16-byte store.
-    constexpr int KC = kTileRows / E;        // key chunks per feature
+    // Transposed V, keys in vt_pos order: storage chunk kc of a feature row
+    // holds the keys vt_pos(kc*E .. kc*E+E-1) of the tile, one 16-byte store
+    // when all of them belong to the frame.
+    constexpr int KC = kTileRows / E;        // storage chunks per feature
     for (int c = tid; c < D * KC; c += 256) {
         const int d = c / KC;
         const int kc = c % KC;
-        const int r = base + kc * E;
         Chunk<T> out;
+        bool full = true;
+        bool valid[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) out.e[e] = vt[(kc * E + e) * LD + d];
-        T* dst = vreg + (static_cast<size_t>(h) * D + d) * rows + r;
-        const int t0 = r - row0;
-        if (t0 >= 0 && t0 + E <= n_tok) {
+        for (int e = 0; e < E; ++e) {
+            const int key = vt_pos(kc * E + e);
+            const int tok = base + key - row0;
+            valid[e] = tok >= 0 && tok < n_tok;
+            full = full && valid[e];
+            out.e[e] = vt[key * LD + d];
+        }
+        T* dst = vreg + (static_cast<size_t>(h) * D + d) * rows + base + kc * E;
+        if (full) {
             *reinterpret_cast<uint4*>(dst) = out.u;
         } else {
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                if (t0 + e >= 0 && t0 + e < n_tok) dst[e] = out.e[e];
+                if (valid[e]) dst[e] = out.e[e];
         }
     }
 }
@@ -143,7 +153,7 @@ __global__ __launch_bounds__(256) void retain_kernel(T* __restrict__ kreg, T* __
     for (int i = threadIdx.x; i < ns * D; i += blockDim.x) {
         const int d = i / ns;
         const int r = i % ns;
-        vh[static_cast<size_t>(d) * rows + dst_row + r] = vh[static_cast<size_t>(d) * rows + src_row + r];
+        vh[static_cast<size_t>(d) * rows + vt_pos(dst_row + r)] = vh[static_cast<size_t>(d) * rows + vt_pos(src_row + r)];
     }
 }
 
@@ -234,7 +244,7 @@ template <typename T, int D>
 hipError_t append_dispatch(int H, int n_tok, int row0, int rows, const void* k, const void* v,
                            void* kreg, void* vreg, void* q, const int32_t* pos, const RopeArgs* rope,
                            int32_t* meta_slot, int32_t frame_id, hipStream_t stream) {
-    const int first = row0 & ~7;
+    const int first = row0 & ~15;
     const int tiles = (row0 + n_tok - first + kTileRows - 1) / kTileRows;
     dim3 grid(tiles, H);
     RopeArgs r{};

@@ -134,7 +134,8 @@ void make_rope(int pt, int ph, int pw, float theta, swa::RopeArgs* r) {
             r->freq[p++] = std::pow(static_cast<double>(theta), -static_cast<double>(kk) / bands[b]);
 }
 
-int tiles_of(int lo, int hi) { return (hi - (lo & ~7) + 63) / 64; }
+// Key tiles of a row segment: 64 rows each, the first starting on a 16-row boundary.
+int tiles_of(int lo, int hi) { return (hi - (lo & ~15) + 63) / 64; }
 
 }  // namespace
 

@@ -140,7 +140,10 @@ def test_cache_bytes_bit_exact():
     torch.cuda.synchronize()
     kr, vr = gc.region_views(0)
     K = kr.float().cpu().numpy()
-    V = vr.float().cpu().numpy()
+    # transposed V keeps key r at position r with bits 2 and 3 swapped
+    r = np.arange(vr.shape[2])
+    vt_pos = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1)
+    V = vr.float().cpu().numpy()[:, :, vt_pos]
     L = gc.layout
     for (f, region, slot, row0, nrows) in gc.pages():
         k, v = frames[f]
