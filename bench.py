@@ -1,17 +1,27 @@
-"""Benchmark of the streaming step on one MI355X.
+"""Benchmarks of the streaming KV-cache attention path on one MI355X.
 
-Default workload (one JSON line): the single streaming step -- P = 1374
-tokens per frame (37x37 patches + 1 camera + 4 register), H = 16, D = 64,
-bf16, 8 scale frames + a 16-frame window, so every step attends 1374
-queries to 24 x 1374 = 32,976 keys.  One step = append (K,V into the ring
-page) + evict + attention (+ split combine), all through the C ABI.
+Default (one JSON line, the headline metric): the single streaming step --
+P = 1374 tokens per frame (37x37 patches + 1 camera + 4 register), H = 16,
+D = 64, bf16, 8 scale frames + a 16-frame window, so each step attends 1374
+queries to 24 x 1374 = 32,976 keys.  One step = append (K and V into the
+frame's ring page) + evict + attention (splits merged in-kernel), through the C ABI.
 
-  value        attention TFLOP/s of the whole step: algorithmic attention
-               FLOPs (4*D*H*sum of visible keys) / measured step time
-  roofline     the attention kernel alone against the bf16 dense MFMA peak
-  cpu_baseline the float64 oracle on the machine's host cores, one steady step
+  value        TFLOP/s of the whole step: algorithmic attention FLOPs
+               (4*D*H*visible query-key pairs) / measured step time
+  roofline     the attention kernel alone (timed with HIP events on the
+               stream it runs on) against the bf16 dense MFMA peak; traffic
+               is the HBM bytes per launch from the FETCH_SIZE/WRITE_SIZE
+               counter summary under profiles/, or null when the kernel
+               sources have changed since those counters were taken
+  cpu_baseline the float64 oracle on the host cores, a few steady steps
 
-Other workloads (--workload prefill|rope|specials) print their own line.
+--workload prefill | rope | specials | all  prints the other workloads:
+  prefill   32 frames at once (43,968 tokens), window 8, 8 scale frames
+  rope      2000 frames streamed with 3-D RoPE, window 6 blocks x 4 frames,
+            8 scale frames (steady state t >= 31)
+  specials  1600 frames, P = 1405 (28x50 + 5), window 16, 8 scale frames,
+            5 special rows of up to 1000 evicted frames retained, every
+            third frame a non-keyframe (append, attend, roll back)
 """
 from __future__ import annotations
 
@@ -24,20 +34,16 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 (published)
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16, published
 HBM_PEAK_GBS = 8000.0
+METRIC = "attention TFLOP/s and frames/s per layer, streaming step (1374 q x ~33k keys)"
 
 
-def _events():
-    import torch
-    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-
-def _timed(fn, steps):
-    """Average ms of fn() over `steps` calls, bracketed by synchronize."""
-    import torch
+def _timed(torch, fn, steps):
+    """Average ms per call of fn(i) over `steps` calls (events on the current stream)."""
     torch.cuda.synchronize()
-    a, b = _events()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
     a.record()
     for i in range(steps):
         fn(i)
@@ -46,38 +52,83 @@ def _timed(fn, steps):
     return a.elapsed_time(b) / steps
 
 
-def cpu_baseline_stream(P, H, D, W, S, frames_fn):
-    """Oracle (float64 NumPy) time of one steady-state step."""
-    import numpy as np
-    from oracle import CacheConfig, NaiveRingCache
-    c = NaiveRingCache(CacheConfig(P=P, sliding_window_size=W, scale_frames=S))
-    for t in range(S + W):
-        q, k, v = frames_fn(t)
-        c.append(t, k, v, True)
-        c.evict()
-    t = S + W
-    q, k, v = frames_fn(t)
-    t0 = time.perf_counter()
-    c.append(t, k, v, True)
-    c.evict()
-    _, _ = c.attend(q)
-    dt = time.perf_counter() - t0
-    keys = sum(p[4] for p in c.visible_pages())
-    return dt, keys
+def _per_step(torch, fn, idx):
+    """Per-call ms of fn(i) for i in idx (one event pair per call)."""
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(idx) + 1)]
+    ev[0].record()
+    for j, i in enumerate(idx):
+        fn(i)
+        ev[j + 1].record()
+    torch.cuda.synchronize()
+    return [ev[j].elapsed_time(ev[j + 1]) for j in range(len(idx))]
 
+
+def _pct(xs, p):
+    s = sorted(xs)
+    return s[min(len(s) - 1, int(round(p / 100.0 * (len(s) - 1))))]
+
+
+def _base(args, metric, value, unit, ms, cfg, dtype="bf16"):
+    return {"metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic: N(0,1) q/k/v rounded to bf16 (seeded per frame)", "config": cfg}
+
+
+def _dev(torch, arrs):
+    return tuple(torch.from_numpy(x).to("cuda").to(torch.bfloat16) for x in arrs)
+
+
+def _cores():
+    return len(os.sched_getaffinity(0))
+
+
+KERNEL_SOURCES = ("sliding_window_kv_amd/csrc/attn_kernels.hip", "sliding_window_kv_amd/csrc/kernels_common.hpp")
+TRAFFIC_SUMMARY = "profiles/attention_stream_traffic.txt"
+
+
+def _sources_sha256(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _measured_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when the kernel sources no longer match the ones it was taken on."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    if fields.get("kernel_sources_sha256") != _sources_sha256(KERNEL_SOURCES):
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# single streaming step (headline)
+# ---------------------------------------------------------------------------
 
 def bench_stream(args, torch, swa):
     from swa_synth import frame_qkv
     P, H, D, W, S = 1374, 16, 64, 16, 8
-    cfg = swa.make_config(P, H, D, sliding_window_size=W, scale_frames=S)
-    cache = swa.SwaCache(cfg)
+    cache = swa.SwaCache(swa.make_config(P, H, D, sliding_window_size=W, scale_frames=S))
     if args.splits is not None:
         cache.set_splits(args.splits)
-    npool = 97 if args.pool is None else args.pool
-    pool = []
-    for i in range(npool):
-        q, k, v = frame_qkv(2, i, P, H, D)
-        pool.append(tuple(torch.from_numpy(x).to("cuda").to(torch.bfloat16) for x in (q, k, v)))
+    npool = 97
+    pool = [_dev(torch, frame_qkv(2, i, P, H, D)) for i in range(npool)]
     out = torch.empty((P, H, D), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((H, P), dtype=torch.float32, device="cuda")
     state = {"t": 0}
@@ -88,56 +139,192 @@ def bench_stream(args, torch, swa):
         cache.step(0, t, q, k, v, True, out, lse)
         state["t"] = t + 1
 
-    # fill the window to the steady state (S + W cached frames), then warm up
-    for _ in range(S + W):
-        step(0)
-    for _ in range(args.warmup):
+    for _ in range(S + W + args.warmup):        # fill the window, then warm up
         step(0)
     keys = sum(p[4] for p in cache.pages())
     assert keys == (S + W) * P
     flops = 4.0 * D * H * P * keys
-
-    ms_step = _timed(step, args.steps)
-    # attention alone (same visible set, no state change)
+    ms_step = _timed(torch, step, args.steps)
     q0 = pool[0][0]
-    ms_attn = _timed(lambda _: cache.attend(0, q0, out, lse), args.steps)
-    # append + evict alone
-    ms_app = _timed(lambda _: (lambda t: (cache.append(0, t, pool[t % npool][1], pool[t % npool][2], True),
-                                          cache.evict(0), state.__setitem__("t", t + 1)))(state["t"]), args.steps)
+    ms_attn = _timed(torch, lambda _: cache.attend(0, q0, out, lse), args.steps)
+
+    def app(_):
+        t = state["t"]
+        cache.append(0, t, pool[t % npool][1], pool[t % npool][2], True)
+        cache.evict(0)
+        state["t"] = t + 1
+
+    ms_app = _timed(torch, app, args.steps)
     append_bytes = 2 * 2 * P * H * D * 2
-    res = {
-        "metric": "attention TFLOP/s and frames/s per layer, streaming step (1374 q x ~33k keys)",
-        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic: N(0,1) q/k/v rounded to bf16, 97 distinct frames cycled",
-        "config": {"workload": "stream_step", "tokens_per_frame": P, "heads": H, "head_dim": D,
-                   "scale_frames": S, "window_frames": W, "visible_keys": keys, "splits": args.splits or "auto"},
+    tflops_attn = flops / (ms_attn * 1e-3) / 1e12
+    res = _base(args, METRIC, flops / (ms_step * 1e-3) / 1e12, "TFLOP/s", ms_step,
+                {"workload": "stream_step", "tokens_per_frame": P, "heads": H, "head_dim": D, "scale_frames": S,
+                 "window_frames": W, "visible_keys": keys, "splits": args.splits or "auto"})
+    res.update({
         "frames_per_s_per_layer": round(1000.0 / ms_step, 1),
-        "attention_ms": round(ms_attn, 4),
-        "append_evict_ms": round(ms_app, 4),
+        "attention_ms": round(ms_attn, 5),
+        "append_evict_ms": round(ms_app, 5),
         "append_GBps": round(append_bytes / (ms_app * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "mfma", "achieved": round(flops / (ms_attn * 1e-3) / 1e12, 2),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(flops / (ms_attn * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None},
-    }
+        "roofline": {"bound": "mfma", "achieved": round(tflops_attn, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops_attn / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": _measured_traffic()},
+    })
     if not args.no_cpu:
-        import numpy as np
-        cores = len(os.sched_getaffinity(0))
-        dt, okeys = cpu_baseline_stream(P, H, D, W, S, lambda t: frame_qkv(2, t % npool, P, H, D))
-        oflops = 4.0 * D * H * P * okeys
-        res["cpu_baseline"] = {"value": round(oflops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
+        from oracle import CacheConfig, NaiveRingCache
+        oc = NaiveRingCache(CacheConfig(P=P, sliding_window_size=W, scale_frames=S))
+        for t in range(S + W):
+            q, k, v = frame_qkv(2, t, P, H, D)
+            oc.append(t, k, v, True)
+            oc.evict()
+        dt, n = 0.0, 0
+        while dt < 10.0 and n < 8:                 # about 10 s of oracle work
+            q, k, v = frame_qkv(2, S + W + n, P, H, D)
+            t0 = time.perf_counter()
+            oc.append(S + W + n, k, v, True)
+            oc.evict()
+            oc.attend(q)
+            dt += time.perf_counter() - t0
+            n += 1
+        res["cpu_baseline"] = {"value": round(n * flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": _cores(),
                                "kind": "oracle",
-                               "sample": f"one steady-state step (append+evict+attend, {okeys} keys), "
-                                         f"{dt:.1f} s, float64 NumPy"}
+                               "sample": f"{n} steady-state steps (append, evict, attend over {keys} keys each), "
+                                         f"{dt:.2f} s in float64 NumPy"}
+    return res
+
+
+# ---------------------------------------------------------------------------
+# chunked masked prefill
+# ---------------------------------------------------------------------------
+
+def bench_prefill(args, torch, swa):
+    import numpy as np
+    from oracle import frame_visibility, masked_attention
+    from swa_synth import chunk_qkv
+    F, P, H, D, W, S = 32, 1374, 16, 64, 8, 8
+    qn, kn, vn = chunk_qkv(3, F, P, H, D)
+    q, k, v = _dev(torch, (qn, kn, vn))
+    out = torch.empty_like(q)
+    need = swa.swa_prefill_workspace_bytes(F, P, H, D, swa.SWA_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    vis = frame_visibility(F, W, 1, S)
+    pairs = int(vis.sum())
+    flops = 4.0 * D * H * P * P * pairs
+    for _ in range(args.warmup):
+        swa.prefill_t(q, k, v, F, P, W, 1, S, out, None, ws)
+    ms = _timed(torch, lambda _: swa.prefill_t(q, k, v, F, P, W, 1, S, out, None, ws), max(1, args.steps // 10))
+    res = _base(args, "prefill attention TFLOP/s (32 frames x 1374 tokens, window 8, 8 scale frames)",
+                flops / (ms * 1e-3) / 1e12, "TFLOP/s", ms,
+                {"workload": "chunked_prefill", "frames": F, "tokens_per_frame": P, "heads": H, "head_dim": D,
+                 "window_frames": W, "scale_frames": S, "visible_frame_pairs": pairs})
+    res["frames_per_s_per_layer"] = round(F * 1000.0 / ms, 1)
+    res["chunk_layout_bytes"] = 2 * 2 * F * P * H * D * 2
+    if not args.no_cpu:
+        # oracle rows of query frames 0, 16 and 31 (1, 16 and 16 visible frames)
+        fk = np.arange(F * P) // P
+        t0 = time.perf_counter()
+        sample_pairs = 0
+        for i in (0, 16, 31):
+            rows = slice(i * P, (i + 1) * P)
+            mask = np.broadcast_to(vis[i][fk][None, :], (P, F * P))
+            masked_attention(qn[rows], kn, vn, mask)
+            sample_pairs += int(vis[i].sum())
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(4.0 * D * H * P * P * sample_pairs / dt / 1e12, 5), "unit": "TFLOP/s",
+                               "cores": _cores(), "kind": "oracle",
+                               "sample": f"query frames 0, 16, 31 ({sample_pairs} frame pairs), {dt:.2f} s"}
+    return res
+
+
+# ---------------------------------------------------------------------------
+# long stream with 3-D RoPE
+# ---------------------------------------------------------------------------
+
+def bench_rope(args, torch, swa):
+    import numpy as np
+    from swa_synth import frame_positions, frame_qkv
+    P, H, D, S = 1374, 16, 64, 8
+    sws, nfpb, T = 6, 4, 2000
+    W = sws * nfpb
+    cache = swa.SwaCache(swa.make_config(P, H, D, sliding_window_size=sws, num_frame_per_block=nfpb,
+                                         scale_frames=S, rope=(12, 10, 10), rope_theta=10000.0))
+    if args.splits is not None:
+        cache.set_splits(args.splits)
+    npool = 97
+    pool = [_dev(torch, frame_qkv(4, i, P, H, D)) for i in range(npool)]
+    pos = torch.from_numpy(np.stack([frame_positions(t, 37, 37, 5) for t in range(T)])).to("cuda")
+    out = torch.empty((P, H, D), dtype=torch.bfloat16, device="cuda")
+
+    def step(t):
+        q, k, v = pool[t % npool]
+        cache.step(0, t, q, k, v, True, out, None, pos=pos[t])
+
+    t0 = S + W - 1                               # 31: cache full from here on
+    for t in range(t0):
+        step(t)
+    times = _per_step(torch, step, list(range(t0, T)))
+    ms = sum(times) / len(times)
+    keys = (S + W) * P
+    flops = 4.0 * D * H * P * keys
+    res = _base(args, "streaming step with 3-D RoPE, TFLOP/s (1374 q x 43,968 keys)",
+                flops / (ms * 1e-3) / 1e12, "TFLOP/s", ms,
+                {"workload": "rope_stream", "frames": T, "tokens_per_frame": P, "heads": H, "head_dim": D,
+                 "window_frames": W, "scale_frames": S, "rope_pairs": [12, 10, 10], "visible_keys": keys,
+                 "timed_steps": f"t in [{t0}, {T})"})
+    res["steps"] = len(times)
+    res["warmup"] = t0
+    res["frames_per_s_per_layer"] = round(1000.0 / ms, 1)
+    res["p50_ms"] = round(_pct(times, 50), 5)
+    res["p99_ms"] = round(_pct(times, 99), 5)
+    res["fused_rope_append_bytes"] = 6 * P * H * D * 2
+    return res
+
+
+# ---------------------------------------------------------------------------
+# ragged frames with retained specials and non-keyframes
+# ---------------------------------------------------------------------------
+
+def bench_specials(args, torch, swa):
+    from swa_synth import frame_qkv
+    P, H, D, W, S, ns, R, T = 1405, 16, 64, 16, 8, 5, 1000, 1600
+    cache = swa.SwaCache(swa.make_config(P, H, D, sliding_window_size=W, scale_frames=S, cross_frame_special=True,
+                                         special_row0=0, special_rows=ns, max_special_frames=R))
+    if args.splits is not None:
+        cache.set_splits(args.splits)
+    npool = 97
+    pool = [_dev(torch, frame_qkv(5, i, P, H, D)) for i in range(npool)]
+    out = torch.empty((P, H, D), dtype=torch.bfloat16, device="cuda")
+    key_of = lambda t: t % 3 != 2          # noqa: E731
+
+    def step(t):
+        q, k, v = pool[t % npool]
+        cache.step(0, t, q, k, v, key_of(t), out, None)
+
+    t0 = 1534
+    for t in range(t0):
+        step(t)
+    idx = list(range(t0, T))
+    times = _per_step(torch, step, idx)
+    kf = [ms for t, ms in zip(idx, times) if key_of(t)]
+    nk = [ms for t, ms in zip(idx, times) if not key_of(t)]
+    ms_k = sum(kf) / len(kf)
+    ms_n = sum(nk) / len(nk)
+    keys_k = (S + W) * P + R * ns
+    keys_n = keys_k + P
+    fl_k = 4.0 * D * H * P * keys_k
+    fl_n = 4.0 * D * H * P * keys_n
+    ms = sum(times) / len(times)
+    res = _base(args, "streaming step with retained specials, TFLOP/s (1405 q x 38,720 / 40,125 keys)",
+                (fl_k * len(kf) + fl_n * len(nk)) / (sum(times) * 1e-3) / 1e12, "TFLOP/s", ms,
+                {"workload": "ragged_specials_stream", "frames": T, "tokens_per_frame": P, "heads": H,
+                 "head_dim": D, "window_frames": W, "scale_frames": S, "special_rows": ns,
+                 "retained_special_frames": R, "nonkeyframe": "t % 3 == 2", "timed_steps": f"t in [{t0}, {T})"})
+    res["steps"] = len(times)
+    res["warmup"] = t0
+    res["keyframe_ms"] = round(ms_k, 5)
+    res["nonkeyframe_ms"] = round(ms_n, 5)
+    res["keyframe_TFLOPs"] = round(fl_k / (ms_k * 1e-3) / 1e12, 2)
+    res["nonkeyframe_TFLOPs"] = round(fl_n / (ms_n * 1e-3) / 1e12, 2)
+    res["frames_per_s_per_layer"] = round(1000.0 / ms, 1)
     return res
 
 
@@ -146,20 +333,22 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="stream", choices=["stream"])
+    ap.add_argument("--workload", default="stream", choices=["stream", "prefill", "rope", "specials", "all"])
     ap.add_argument("--splits", type=int, default=None)
-    ap.add_argument("--pool", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print("this build runs on one GPU only: use --gpus 1 (the head-sharded multi-GPU layout is design only)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     import sliding_window_kv_amd as swa
     swa.lib()
     torch.cuda.set_device(0)
-    res = bench_stream(args, torch, swa)
-    print(json.dumps(res), flush=True)
+    order = ["stream", "prefill", "rope", "specials"] if args.workload == "all" else [args.workload]
+    fns = {"stream": bench_stream, "prefill": bench_prefill, "rope": bench_rope, "specials": bench_specials}
+    for w in order:
+        print(json.dumps(fns[w](args, torch, swa)), flush=True)
 
 
 if __name__ == "__main__":

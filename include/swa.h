@@ -128,6 +128,8 @@ typedef struct swa_page {
  *       lane's operand).
  * Page slot s holds a frame in rows [s*P, (s+1)*P); special-ring entry e
  * holds its rows at special_row_base + e*special_rows.
+ * The work area [work_offset, work_offset + work_bytes) holds the partial
+ * results of streaming attention calls; it is scratch between calls.
  */
 typedef struct swa_layout {
     int64_t layer_bytes;
@@ -151,8 +153,9 @@ size_t swa_cache_pool_bytes(const swa_config* cfg);
 
 /*
  * Create a cache over a caller-owned device pool of at least
- * swa_cache_pool_bytes(cfg) bytes (256-byte aligned).  The library owns only
- * host-side bookkeeping.  dev_pool = NULL with pool_bytes = 0 makes a
+ * swa_cache_pool_bytes(cfg) bytes (256-byte aligned).  The library keeps its
+ * bookkeeping on the host and allocates no device memory; the pool's
+ * contents need no initialisation.  dev_pool = NULL with pool_bytes = 0 makes a
  * bookkeeping-only cache: append/evict/rollback/reset and
  * kvcache_visible_pages work and enqueue nothing; every call that would touch
  * the device returns SWA_E_STATE.
@@ -161,7 +164,15 @@ int swa_cache_create(const swa_config* cfg, void* dev_pool, size_t pool_bytes, s
 int swa_cache_destroy(swa_cache* cache);
 int swa_cache_layout(const swa_cache* cache, swa_layout* out);
 
-/* KV splits used by the streaming attention (0 = automatic, else 1..32). */
+/*
+ * Work split of the streaming bf16 attention.  0 (default): the
+ * num_heads * n (head, key tile) space is cut into as many equal columns as
+ * the GPU runs at once (one launch round, every work-group the same number
+ * of tiles); pieces of heads cut by a column edge are merged by a second
+ * kernel.  k >= 1: each head's key tiles are cut into k equal pieces
+ * (k = 1: no partials, no merge); num_heads * k is capped at 256.
+ * SWA_E_INVAL for k outside 0..256.
+ */
 int swa_cache_set_splits(swa_cache* cache, int splits);
 
 /* Forget every cached frame of every layer ([G] "Cache Reset Between

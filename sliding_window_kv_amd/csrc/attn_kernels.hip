@@ -40,6 +40,10 @@ namespace {
 
 constexpr int KT = 64;            // keys per tile
 constexpr int KALIGN = 16;        // tile start alignment (rows)
+#ifndef SWA_RING
+#define SWA_RING 3
+#endif
+constexpr int kRing = SWA_RING;   // K/V tile buffers of the straightforward kernel
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -139,44 +143,12 @@ __device__ __forceinline__ int lds_swz(int row) {
     return (row / (16 / CPR)) % CPR;
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Direct global->LDS loads of one tile (16 bytes per lane; a wave
-// instruction fills 64 consecutive 16-byte LDS chunks).  LDS chunk p of the
-// K buffer holds row p / CPR, feature chunk (p % CPR) ^ lds_swz(row); chunk
-// p of the V^T buffer holds feature row p / 8, key chunk (p % 8) ^ lds_swz(row).
-template <int D, int NW>
-__device__ __forceinline__ void tile_load_lds(const uint16_t* kh, const uint16_t* vh, int rows, int base,
-                                              uint16_t* ks, uint16_t* vs, int wave, int lane) {
-    constexpr int CPR = D / 8;
-    constexpr int NK = KT * CPR / (64 * NW);
-    constexpr int NV = D * (KT / 8) / (64 * NW);
-    static_assert(NK * 64 * NW == KT * CPR && NV * 64 * NW == D * (KT / 8), "tile/wave mismatch");
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-        const int p0 = (i * NW + wave) * 64;
-        const int p = p0 + lane;
-        const int row = p / CPR;
-        const int dc = (p % CPR) ^ lds_swz<CPR>(row);
-        const uint16_t* g = kh + static_cast<size_t>(base + row) * D + dc * 8;
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                         (__attribute__((address_space(3))) void*)(ks + p0 * 8), 16, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int p0 = (i * NW + wave) * 64;
-        const int p = p0 + lane;
-        const int d = p / 8;
-        const int kc = (p % 8) ^ lds_swz<8>(d);
-        const uint16_t* g = vh + static_cast<size_t>(d) * rows + base + kc * 8;
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                         (__attribute__((address_space(3))) void*)(vs + p0 * 8), 16, 0, 0);
-    }
-}
-
 // Clear the V^T elements of keys outside [c.lo, c.hi) in a landed tile.
 template <int D, int NT>
 __device__ __forceinline__ void tile_clear_edges(uint16_t* vs, const Cursor& c, int tid) {
+    // rare path: keep its per-thread addresses out of loop-invariant code
+    // motion, which would hold one register per buffer and element
+    asm volatile("" : "+v"(tid));
     for (int e = tid; e < D * KT; e += NT) {
         const int d = e / KT;
         const int pos = e % KT;                      // storage position in the tile
@@ -185,45 +157,6 @@ __device__ __forceinline__ void tile_clear_edges(uint16_t* vs, const Cursor& c, 
             const int kc = pos / 8;
             vs[d * KT + ((kc ^ lds_swz<8>(d)) * 8) + pos % 8] = 0;
         }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Software-pipelined bf16 kernel (one wave per SIMD).  Iteration j runs the
-// softmax of tile j on the vector ALUs while the matrix cores compute
-// S_{j+1} = K_{j+1} Q^T and O += V_{j-1} P_{j-1}; the two streams are
-// interleaved instruction by instruction with scheduling barriers.  K and
-// V^T tiles are double-buffered and loaded one iteration ahead.
-// ---------------------------------------------------------------------------
-
-template <int D, int NW>
-__device__ __forceinline__ void load_k_lds(const uint16_t* kh, int base, uint16_t* ks, int wave, int lane) {
-    constexpr int CPR = D / 8;
-    constexpr int NK = KT * CPR / (64 * NW);
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-        const int p0 = (i * NW + wave) * 64;
-        const int p = p0 + lane;
-        const int row = p / CPR;
-        const int dc = (p % CPR) ^ lds_swz<CPR>(row);
-        const uint16_t* g = kh + static_cast<size_t>(base + row) * D + dc * 8;
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                         (__attribute__((address_space(3))) void*)(ks + p0 * 8), 16, 0, 0);
-    }
-}
-
-template <int D, int NW>
-__device__ __forceinline__ void load_v_lds(const uint16_t* vh, int rows, int base, uint16_t* vs, int wave, int lane) {
-    constexpr int NV = D * (KT / 8) / (64 * NW);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int p0 = (i * NW + wave) * 64;
-        const int p = p0 + lane;
-        const int d = p / 8;
-        const int kc = (p % 8) ^ lds_swz<8>(d);
-        const uint16_t* g = vh + static_cast<size_t>(d) * rows + base + kc * 8;
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                         (__attribute__((address_space(3))) void*)(vs + p0 * 8), 16, 0, 0);
     }
 }
 
@@ -253,163 +186,12 @@ __device__ __forceinline__ float xhalf_sum(float x) {
     return a + b;
 }
 
-template <int D, int QB, bool DO_S, bool DO_PV>
-__device__ __forceinline__ void pipe_step(f32x16 (&s)[2][QB], bf16x8 (&pcur)[2][QB][2], const bf16x8 (&pprev)[2][QB][2],
-                                          f32x16 (&o)[QB][D / 32], float (&m)[QB], float (&l)[QB],
-                                          const bf16x8 (&qf)[QB][D / 16], const uint16_t* kb_lds,
-                                          const uint16_t* vb_lds, const Cursor& cs, float sl2, int l32, int hl) {
-    constexpr int CPR = D / 8;
-    constexpr int KS = D / 16;
-    constexpr int DB = D / 32;
-    static_assert(QB == 1 || QB == 2, "one or two query blocks per wave");
-    constexpr int NB = 2 * QB;                   // 32x32 score blocks per tile
-    constexpr int PPB = 4 / NB;                  // PV 16-key steps per block
-    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-    const int ksw = lds_swz<CPR>(l32);
-    const int vsw = lds_swz<8>(l32);
-
-    // keys outside the segment get -inf (first/last tile of a segment only)
-    if (cs.base < cs.lo || cs.base + KT > cs.hi) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = cs.base + kb * 32 + 8 * (i >> 2) + 4 * hl + (i & 3);
-                if (key < cs.lo || key >= cs.hi) {
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) s[kb][qb][i] = -INFINITY;
-                }
-            }
-    }
-
-    // row max of tile j, running max, rescale factor
-    float mnew[QB], alpha[QB];
-    bool need = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        float mx = s[0][qb][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][qb][i]);
-        mx = xhalf_max(mx);
-        mnew[qb] = fmaxf(m[qb], mx * sl2);
-        alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mnew[qb]);
-        need = need || (__builtin_amdgcn_ballot_w64(mnew[qb] > m[qb]) != 0);
-        l[qb] *= alpha[qb];
-        m[qb] = mnew[qb];
-    }
-
-    const f32x16 zero16 = {};
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        const int kb = b / QB;                   // block of tile j / S_{j+1}
-        const int qb = b % QB;
-        u32x4 ka[KS];
-        if constexpr (DO_S) {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int row = kb * 32 + l32;
-                ka[ks] = *reinterpret_cast<const u32x4*>(kb_lds + (row * CPR + ((ks * 2 + hl) ^ ksw)) * 8);
-            }
-        }
-        u32x4 va[PPB][DB];
-        if constexpr (DO_PV) {
-#pragma unroll
-            for (int pp = 0; pp < PPB; ++pp) {
-                const int pr = b * PPB + pp;     // PV step (kbv, hfv) = 16 keys of tile j-1
-                const int kbv = pr / 2;
-                const int hfv = pr % 2;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const int d = db * 32 + l32;
-                    const int kc = kbv * 4 + hfv * 2 + hl;
-                    va[pp][db] = *reinterpret_cast<const u32x4*>(vb_lds + d * KT + ((kc ^ vsw) * 8));
-                }
-            }
-        }
-        // softmax of block (kb, qb) of tile j
-        float ls = l[qb];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            uint32_t w[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][hf * 8 + 2 * e], sl2, -mnew[qb]));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][hf * 8 + 2 * e + 1], sl2, -mnew[qb]));
-                w[e] = pack_bf2(p0, p1);
-                ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, ls, false);
-            }
-            pcur[kb][qb][hf] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-        }
-        l[qb] = ls;
-        // S_{j+1} for the same block, in the registers just consumed
-        if constexpr (DO_S) {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[ks]), qf[qb][ks],
-                                                                    ks == 0 ? zero16 : s[kb][qb], 0, 0, 0);
-        }
-        // this block's share of O += V_{j-1} P_{j-1}
-        if constexpr (DO_PV) {
-#pragma unroll
-            for (int pp = 0; pp < PPB; ++pp) {
-                const int pr = b * PPB + pp;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int q2 = 0; q2 < QB; ++q2)
-                        o[q2][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, va[pp][db]), pprev[pr / 2][q2][pr % 2], o[q2][db], 0, 0, 0);
-            }
-        }
-        constexpr int NM = (DO_S ? KS : 0) + (DO_PV ? PPB * DB * QB : 0);
-        constexpr int ND = (DO_S ? KS : 0) + (DO_PV ? PPB * DB : 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, ND, 0);
-#pragma unroll
-        for (int i = 0; i < NM; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 48 / NM, 0);
-        }
-    }
-
-    // O holds tiles up to j-1 relative to the previous max: bring it to m_j
-    if (need) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) o[qb][db][i] *= alpha[qb];
-    }
-}
-
-// Final O += V_{n-1} P_{n-1}.
-template <int D, int QB>
-__device__ __forceinline__ void pipe_last_pv(const bf16x8 (&pp)[2][QB][2], f32x16 (&o)[QB][D / 32],
-                                             const uint16_t* vb_lds, int l32, int hl) {
-    constexpr int DB = D / 32;
-    const int vsw = lds_swz<8>(l32);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int d = db * 32 + l32;
-                const int kc = kb * 4 + hf * 2 + hl;
-                const u32x4 a = *reinterpret_cast<const u32x4*>(vb_lds + d * KT + ((kc ^ vsw) * 8));
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pp[kb][qb][hf],
-                                                                        o[qb][db], 0, 0, 0);
-            }
-}
-
-// Final normalisation (split == 1) or the split partials (split > 1).
+// Epilogue of one work item: the normalised output and LSE (piece < 0), or
+// the un-normalised partial (O, m, l) of a key range in slot `piece` of the
+// work area, for the merge kernel.
 template <int D, int QB, bool PREFILL>
 __device__ __forceinline__ void write_out(const AttnParams& p, const f32x16 (&o)[QB][D / 32], const float (&m)[QB],
-                                          const float (&l)[QB], int qrow0, int frame, int h, int split, int l32,
+                                          const float (&l)[QB], int qrow0, int frame, int h, int piece, int l32,
                                           int hl) {
     constexpr int DB = D / 32;
 #pragma unroll
@@ -417,7 +199,7 @@ __device__ __forceinline__ void write_out(const AttnParams& p, const f32x16 (&o)
         const float lt = xhalf_sum(l[qb]);
         const int r = qrow0 + qb * 32 + l32;
         if (r >= p.nq) continue;
-        if (p.splits == 1) {
+        if (piece < 0) {
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
             const size_t g = (static_cast<size_t>(frame) * p.nq + r) * p.H + h;
             uint16_t* dst = static_cast<uint16_t*>(p.out) + g * D;
@@ -434,7 +216,7 @@ __device__ __forceinline__ void write_out(const AttnParams& p, const f32x16 (&o)
                 p.lse[static_cast<size_t>(h) * p.nq * (PREFILL ? p.F : 1) + static_cast<size_t>(frame) * p.nq + r] =
                     (m[qb] + log2f(lt)) * 0.69314718055994530942f;
         } else {
-            const size_t row = (static_cast<size_t>(split) * p.H + h) * p.nq + r;
+            const size_t row = static_cast<size_t>(piece) * p.nq + r;
             float* dst = p.part_o + row * D;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
@@ -496,33 +278,64 @@ __device__ __forceinline__ void tile_load(const TileOffsets<D, NW>& off, const u
                                          (__attribute__((address_space(3))) void*)(vs + (i * NW + wave) * 512), 16, 0, 0);
 }
 
-// One tile of the straightforward schedule: S^T = K Q^T, online softmax,
-// O^T += V^T P^T, all from the landed buffers (ks, vs) of tile `cur`.
-template <int D, int QB>
-__device__ __forceinline__ void basic_tile(const uint16_t* ks, const uint16_t* vs, const Cursor& cur,
-                                           const bf16x8 (&qf)[QB][D / 16], f32x16 (&o)[QB][D / 32], float (&m)[QB],
-                                           float (&l)[QB], float sl2, int l32, int hl) {
-    constexpr int CPR = D / 8;
-    constexpr int KS = D / 16;
-    constexpr int DB = D / 32;
-    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-    const int ksw = lds_swz<CPR>(l32);
-    const int vsw = lds_swz<8>(l32);
+// The three phases of one 64-key tile for one wave.  LDS reads address a
+// tile as slot base + per-lane part (+ a constant for the second 32-row
+// half); the per-lane parts come precomputed (TileLanes), so a kernel with
+// many slots does not keep one address register per slot and read.
+template <int D>
+struct TileLanes {
+    static constexpr int KS = D / 16;
+    int k[KS];               // K tile: row l32, chunk (2*ks + hl) ^ swizzle, in elements
+    int v[4];                // V^T tile: row l32, chunk (4*kb + 2*hf + hl) ^ swizzle
+    __device__ TileLanes(int l32, int hl) {
+        constexpr int CPR = D / 8;
+        const int ksw = lds_swz<CPR>(l32);
+        const int vsw = lds_swz<8>(l32);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) k[ks] = (l32 * CPR + ((ks * 2 + hl) ^ ksw)) * 8;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) v[x] = l32 * KT + ((x * 2 + hl) ^ vsw) * 8;
+    }
+    // Hide the values from loop-invariant code motion: added to each slot's
+    // constant base at the read, not hoisted as one register per slot.
+    __device__ __forceinline__ void refresh() {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(k[ks]));
+#pragma unroll
+        for (int x = 0; x < 4; ++x) asm volatile("" : "+v"(v[x]));
+    }
+};
 
-    f32x16 s[2][QB];
+// Scores: S^T = K Q^T (MFMA; the accumulator of lane l, register i holds
+// key 8*(i/4) + 4*(l/32) + i%4 of each 32-key half and query l%32).
+template <int D, int QB>
+__device__ __forceinline__ void tile_scores(const uint16_t* ks, const bf16x8 (&qf)[QB][D / 16], f32x16 (&s)[2][QB],
+                                            const TileLanes<D>& tl) {
+    constexpr int KS = D / 16;
     const f32x16 zero16 = {};
 #pragma unroll
     for (int ks_ = 0; ks_ < KS; ++ks_) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const int row = kb * 32 + l32;
-            const u32x4 a = *reinterpret_cast<const u32x4*>(ks + (row * CPR + ((ks_ * 2 + hl) ^ ksw)) * 8);
+            const u32x4 a = *reinterpret_cast<const u32x4*>(ks + kb * 32 * D + tl.k[ks_]);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
                 s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[qb][ks_],
                                                                     ks_ == 0 ? zero16 : s[kb][qb], 0, 0, 0);
         }
     }
+}
+
+// Online softmax (vector ALUs): keys outside the tile's segment get -inf;
+// new running max m (log2 domain), O and l rescaled when any lane's max
+// moved; P = 2^(s*scale - m) rounded to bf16 into the B operand of the PV
+// product, and l accumulates exactly those bf16 values.
+template <int D, int QB>
+__device__ __forceinline__ void tile_softmax(f32x16 (&s)[2][QB], const Cursor& cur, bf16x8 (&pb)[2][QB][2],
+                                             f32x16 (&o)[QB][D / 32], float (&m)[QB], float (&l)[QB], float sl2,
+                                             int hl) {
+    constexpr int DB = D / 32;
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
     if (cur.base < cur.lo || cur.base + KT > cur.hi) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -535,7 +348,6 @@ __device__ __forceinline__ void basic_tile(const uint16_t* ks, const uint16_t* v
                 }
             }
     }
-    bf16x8 pb[2][QB][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         float mx = s[0][qb][0];
@@ -571,15 +383,21 @@ __device__ __forceinline__ void basic_tile(const uint16_t* ks, const uint16_t* v
             }
         l[qb] = ls;
     }
+}
+
+// O^T += V^T P^T (MFMA); V^T rows hold keys in vt_pos order, so one 16-byte
+// LDS read per lane is the A operand matching P's register layout.
+template <int D, int QB>
+__device__ __forceinline__ void tile_pv(const uint16_t* vs, const bf16x8 (&pb)[2][QB][2], f32x16 (&o)[QB][D / 32],
+                                        const TileLanes<D>& tl) {
+    constexpr int DB = D / 32;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const int d = db * 32 + l32;
-                const int kc = kb * 4 + hf * 2 + hl;
-                const u32x4 a = *reinterpret_cast<const u32x4*>(vs + d * KT + ((kc ^ vsw) * 8));
+                const u32x4 a = *reinterpret_cast<const u32x4*>(vs + db * 32 * KT + tl.v[kb * 2 + hf]);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
                     o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb[kb][qb][hf],
@@ -587,79 +405,127 @@ __device__ __forceinline__ void basic_tile(const uint16_t* ks, const uint16_t* v
             }
 }
 
-// One iteration of the straightforward kernel: wait for tile `it`, clear its
-// edge keys, start the loads of the next tile into the other buffers, then
-// compute.  Buffers are distinct LDS variables chosen at compile time, so
-// the direct loads are known not to alias the reads of this tile.
-template <int D, int NW, int QB, class Src>
-__device__ __forceinline__ void basic_iter(int it, int ntiles, Cursor& cur, Cursor& nxt, const Src& segs,
-                                           const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
-                                           uint16_t* kcur, uint16_t* vcur, uint16_t* knext, uint16_t* vnext,
+// One tile of the straightforward schedule, all three phases in order.
+template <int D, int QB>
+__device__ __forceinline__ void basic_tile(const uint16_t* ks, const uint16_t* vs, const Cursor& cur,
                                            const bf16x8 (&qf)[QB][D / 16], f32x16 (&o)[QB][D / 32], float (&m)[QB],
-                                           float (&l)[QB], float sl2, int tid) {
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    __syncthreads();                             // tile `it` landed; tile it-1 fully consumed
-    if (cur.base < cur.lo || cur.base + KT > cur.hi) {
-        tile_clear_edges<D, NW * 64>(vcur, cur, tid);
-        __syncthreads();
-    }
-    if (it + 1 < ntiles) {
-        cursor_next(segs, &nxt);
-        tile_load<D, NW>(off, kh, vh, nxt.base, knext, vnext, wave);
-    }
-    basic_tile<D, QB>(kcur, vcur, cur, qf, o, m, l, sl2, lane & 31, lane >> 5);
-    cur = nxt;
+                                           float (&l)[QB], float sl2, int l32, int hl) {
+    f32x16 s[2][QB];
+    bf16x8 pb[2][QB][2];
+    const TileLanes<D> tl(l32, hl);
+    tile_scores<D, QB>(ks, qf, s, tl);
+    tile_softmax<D, QB>(s, cur, pb, o, m, l, sl2, hl);
+    tile_pv<D, QB>(vs, pb, o, tl);
 }
 
-template <int D, int NW, int QB, int OCC, bool PREFILL>
-__global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnParams p) {
+// Work-group barrier after this wave's LDS accesses and all but its N
+// youngest vector-memory operations have completed (loads return in order,
+// so the older direct-to-LDS tiles have landed).  Written out rather than
+// __syncthreads(): the fences of that one made the compiler wait for every
+// load in flight, the prefetched tiles included.
+template <int N>
+__device__ __forceinline__ void sync_tiles() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+    __builtin_amdgcn_sched_barrier(0);           // no instruction moves across the barrier
+}
+
+// K/V tile ring of NB buffers: tile t lives in buffer t % NB and is loaded
+// NB - 1 iterations ahead of its use.  One iteration (buffer U = it % NB):
+// wait for tile `it` (the NB - 2 younger tiles may stay in flight), barrier
+// (publishes tile `it`, and every wave is done with tile it - 1, whose
+// buffer is refilled next), clear its edge keys, start loading tile
+// it + NB - 1, then compute.  U is a compile-time constant and every buffer
+// is an LDS variable of its own, so the compiler can tell the buffer being
+// read from the ones being loaded (with one array it waited for all loads).
+template <int D, int NW, int QB, int NB, int U, class Src>
+__device__ __forceinline__ void ring_iter(int it, int ntiles, Cursor (&cq)[NB], Cursor& ld, const Src& segs,
+                                          const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
+                                          uint16_t* const (&kbuf)[4], uint16_t* const (&vbuf)[4], const bf16x8 (&qf)[QB][D / 16],
+                                          f32x16 (&o)[QB][D / 32], float (&m)[QB], float (&l)[QB], float sl2,
+                                          int tid) {
+    using TO = TileOffsets<D, NW>;
+    constexpr int PER_TILE = TO::NK + TO::NV;    // load instructions per wave per tile
+    constexpr int NXT = (U + NB - 1) % NB;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    if (it + NB - 2 < ntiles)
+        sync_tiles<(NB - 2) * PER_TILE>();
+    else
+        sync_tiles<0>();
+    const Cursor cur = cq[U];
+    uint16_t* kcur = kbuf[U];
+    uint16_t* vcur = vbuf[U];
+    if (cur.base < cur.lo || cur.base + KT > cur.hi) {
+        tile_clear_edges<D, NW * 64>(vcur, cur, tid);
+        sync_tiles<63>();
+    }
+    if (it + NB - 1 < ntiles) {
+        cursor_next(segs, &ld);
+        cq[NXT] = ld;
+        tile_load<D, NW>(off, kh, vh, ld.base, kbuf[NXT], vbuf[NXT], wave);
+    }
+    basic_tile<D, QB>(kcur, vcur, cur, qf, o, m, l, sl2, lane & 31, lane >> 5);
+}
+
+template <int D, int NW, int QB, int NB, int U, class Src>
+__device__ __forceinline__ void ring_tail(int it, int ntiles, Cursor (&cq)[NB], Cursor& ld, const Src& segs,
+                                          const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
+                                          uint16_t* const (&kbuf)[4], uint16_t* const (&vbuf)[4], const bf16x8 (&qf)[QB][D / 16],
+                                          f32x16 (&o)[QB][D / 32], float (&m)[QB], float (&l)[QB], float sl2,
+                                          int tid) {
+    if constexpr (U < NB) {
+        if (it < ntiles) {
+            ring_iter<D, NW, QB, NB, U>(it, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, qf, o, m, l, sl2, tid);
+            ring_tail<D, NW, QB, NB, U + 1>(it + 1, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, qf, o, m, l, sl2,
+                                            tid);
+        }
+    }
+}
+
+template <int D, int NW, int QB, int NB, int U, class Src>
+__device__ __forceinline__ void ring_round(int it, int ntiles, Cursor (&cq)[NB], Cursor& ld, const Src& segs,
+                                           const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
+                                           uint16_t* const (&kbuf)[4], uint16_t* const (&vbuf)[4], const bf16x8 (&qf)[QB][D / 16],
+                                           f32x16 (&o)[QB][D / 32], float (&m)[QB], float (&l)[QB], float sl2,
+                                           int tid) {
+    if constexpr (U < NB) {
+        ring_iter<D, NW, QB, NB, U>(it + U, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, qf, o, m, l, sl2, tid);
+        ring_round<D, NW, QB, NB, U + 1>(it, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, qf, o, m, l, sl2, tid);
+    }
+}
+
+// One work item: query tile `qt` of (frame, head h) against key tiles
+// [t_begin, t_end) of the segment list, finished by write_out(piece).
+template <int D, int NW, int QB, bool PREFILL>
+__device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<PREFILL>& segs, int h, int frame,
+                                             int qt, int t_begin, int t_end, int piece, uint16_t* const (&KB)[4],
+                                             uint16_t* const (&VB)[4], int tid) {
     using Sh = Shape<NW, QB>;
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
-
-    __shared__ __attribute__((aligned(16))) uint16_t K0[KT * D];
-    __shared__ __attribute__((aligned(16))) uint16_t K1[KT * D];
-    __shared__ __attribute__((aligned(16))) uint16_t V0[D * KT];
-    __shared__ __attribute__((aligned(16))) uint16_t V1[D * KT];
-
-    const int tid = threadIdx.x;
+    constexpr int NB = kRing;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int l32 = lane & 31;
     const int hl = lane >> 5;
-
-    // ---- work item ------------------------------------------------------------
-    const int G = gridDim.x;
-    const int L = xcd_remap(blockIdx.x, G);
-    const int qt = L % p.qtiles;
-    const int grp = L / p.qtiles;
-    int h, split, frame;
-    PreSegs pre{};
-    if constexpr (PREFILL) {
-        h = grp % p.H;
-        frame = p.F - 1 - grp / p.H;             // heaviest frames first
-        split = 0;
-        pre = prefill_segs(frame, p.W, p.S, p.fP);
-    } else {
-        h = grp / p.splits;
-        split = grp % p.splits;
-        frame = 0;
-    }
-    const SegSrc<PREFILL> segs{p, pre};
-    const int t_begin = static_cast<int>((static_cast<int64_t>(segs.total()) * split) / p.splits);
-    const int t_end = static_cast<int>((static_cast<int64_t>(segs.total()) * (split + 1)) / p.splits);
     const int ntiles = t_end - t_begin;
 
     const uint16_t* kh = static_cast<const uint16_t*>(p.kreg) + static_cast<size_t>(h) * p.rows * D;
     const uint16_t* vh = static_cast<const uint16_t*>(p.vreg) + static_cast<size_t>(h) * D * p.rows;
     const TileOffsets<D, NW> off(p.rows, wave, lane);
 
-    Cursor cur = cursor_at(segs, t_begin);
-    Cursor nxt = cur;
-    if (ntiles > 0) tile_load<D, NW>(off, kh, vh, cur.base, K0, V0, wave);
+    // prologue: tiles 0 .. NB-2 in flight
+    Cursor cq[NB];
+    Cursor ld = cursor_at(segs, t_begin);
+#pragma unroll
+    for (int u = 0; u < NB - 1; ++u) {
+        if (u > 0) cursor_next(segs, &ld);
+        cq[u] = ld;
+        if (u < ntiles) tile_load<D, NW>(off, kh, vh, ld.base, KB[u], VB[u], wave);
+    }
 
-    // ---- Q^T operands ----------------------------------------------------------
+    // Q^T operands
     const int qrow0 = qt * Sh::QROWS + wave * QB * 32;
     bf16x8 qf[QB][KS];
 #pragma unroll
@@ -689,184 +555,113 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnParams p) {
     const float sl2 = p.scale_log2;
 
     int it = 0;
-    for (; it + 1 < ntiles; it += 2) {
-        basic_iter<D, NW, QB>(it, ntiles, cur, nxt, segs, off, kh, vh, K0, V0, K1, V1, qf, o, m, l, sl2, tid);
-        basic_iter<D, NW, QB>(it + 1, ntiles, cur, nxt, segs, off, kh, vh, K1, V1, K0, V0, qf, o, m, l, sl2, tid);
-    }
-    if (it < ntiles)
-        basic_iter<D, NW, QB>(it, ntiles, cur, nxt, segs, off, kh, vh, K0, V0, K1, V1, qf, o, m, l, sl2, tid);
+    for (; it + NB <= ntiles; it += NB)
+        ring_round<D, NW, QB, NB, 0>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, qf, o, m, l, sl2, tid);
+    ring_tail<D, NW, QB, NB, 0>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, qf, o, m, l, sl2, tid);
 
-    write_out<D, QB, PREFILL>(p, o, m, l, qrow0, frame, h, split, l32, hl);
+    write_out<D, QB, PREFILL>(p, o, m, l, qrow0, frame, h, piece, l32, hl);
 }
 
-
-// One pipeline iteration j with static buffer roles: K_t lives in buffer
-// t % 2 and V_t in buffer t % 2.  The iteration reads K_{j+1} (kr) and
-// V_{j-1} (vr) and fills the other buffers (kw, vw) with K_{j+2} and V_j.
-// Using distinct LDS variables per buffer lets the compiler see that the
-// direct loads never alias the reads, so no wait is inserted between them.
-template <int D, int NW, int QB, class Src>
-__device__ __forceinline__ void pipe_iter(int j, int n, f32x16 (&sreg)[2][QB], bf16x8 (&pcur)[2][QB][2],
-                                          const bf16x8 (&pprev)[2][QB][2], Cursor& cm1, Cursor& c0, Cursor& c1,
-                                          Cursor& c2, const Src& segs, f32x16 (&o)[QB][D / 32], float (&m)[QB],
-                                          float (&l)[QB], const bf16x8 (&qf)[QB][D / 16], const uint16_t* kr,
-                                          uint16_t* vr, uint16_t* kw, uint16_t* vw, const uint16_t* kh,
-                                          const uint16_t* vh, int rows, float sl2, int tid) {
-    constexpr int NT = NW * 64;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int l32 = lane & 31;
-    const int hl = lane >> 5;
-    __syncthreads();                                   // K_{j+1}, V_{j-1} landed; K_j, V_{j-2} consumed
-    if (j > 0 && (cm1.base < cm1.lo || cm1.base + KT > cm1.hi)) {
-        tile_clear_edges<D, NT>(vr, cm1, tid);
-        __syncthreads();
-    }
-    // loads one iteration ahead (past the last tile: reload the last one)
-    load_k_lds<D, NW>(kh, c2.base, kw, wave, lane);
-    load_v_lds<D, NW>(vh, rows, c0.base, vw, wave, lane);
-    pipe_step<D, QB, true, true>(sreg, pcur, pprev, o, m, l, qf, kr, vr, c0, sl2, l32, hl);
-    cm1 = c0;
-    c0 = c1;
-    c1 = c2;
-    if (j + 3 < n) cursor_next(segs, &c2);
-}
-
+// Work decomposition.  Prefill: one work item per (frame, head, query tile).
+// Streaming: every query of the frame sees the same key tiles, so the
+// (head, key tile) space of H * n tiles is cut into p.ncols equal columns,
+// and column c runs as p.qtiles work-groups, one per query tile, that walk
+// the same K/V tiles at the same time (consecutive work-groups: one XCD and
+// its L2).  A column's range may end and start inside heads; such pieces go
+// to the work area as partials (slot 2c for the column's first head, 2c + 1
+// for its last) and the merge kernel combines them.  With ncols near
+// (work-groups the GPU holds) / qtiles, every work-group gets the same
+// number of tiles and the launch finishes in one round.
 template <int D, int NW, int QB, int OCC, bool PREFILL>
-__global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_pipe_kernel(AttnParams p) {
-    using Sh = Shape<NW, QB>;
-    constexpr int NT = Sh::NT;
-    constexpr int CPR = D / 8;
-    constexpr int KS = D / 16;
-    constexpr int DB = D / 32;
+__global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnParams p) {
+    constexpr int NB = kRing;
+    static_assert(NB >= 2 && NB <= 4, "2 to 4 tile buffers");
 
     __shared__ __attribute__((aligned(16))) uint16_t K0[KT * D];
     __shared__ __attribute__((aligned(16))) uint16_t K1[KT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t K2[NB > 2 ? KT * D : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t K3[NB > 3 ? KT * D : 8];
     __shared__ __attribute__((aligned(16))) uint16_t V0[D * KT];
     __shared__ __attribute__((aligned(16))) uint16_t V1[D * KT];
+    __shared__ __attribute__((aligned(16))) uint16_t V2[NB > 2 ? D * KT : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t V3[NB > 3 ? D * KT : 8];
+    uint16_t* const KB[4] = {K0, K1, K2, K3};
+    uint16_t* const VB[4] = {V0, V1, V2, V3};
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int l32 = lane & 31;
-    const int hl = lane >> 5;
-
-    // ---- work item ------------------------------------------------------------
-    const int G = gridDim.x;
-    const int L = xcd_remap(blockIdx.x, G);
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
     const int qt = L % p.qtiles;
-    const int grp = L / p.qtiles;
-    int h, split, frame;
-    PreSegs pre{};
+    const int item = L / p.qtiles;
     if constexpr (PREFILL) {
-        h = grp % p.H;
-        frame = p.F - 1 - grp / p.H;
-        split = 0;
-        pre = prefill_segs(frame, p.W, p.S, p.fP);
+        const int h = item % p.H;
+        const int frame = p.F - 1 - item / p.H;          // heaviest frames first
+        const SegSrc<true> segs{p, prefill_segs(frame, p.W, p.S, p.fP)};
+        attend_range<D, NW, QB, true>(p, segs, h, frame, qt, 0, segs.total(), -1, KB, VB, tid);
     } else {
-        h = grp / p.splits;
-        split = grp % p.splits;
-        frame = 0;
-    }
-    const SegSrc<PREFILL> segs{p, pre};
-    const int t_begin = static_cast<int>((static_cast<int64_t>(segs.total()) * split) / p.splits);
-    const int t_end = static_cast<int>((static_cast<int64_t>(segs.total()) * (split + 1)) / p.splits);
-    const int n = t_end - t_begin;
-
-    const uint16_t* kh = static_cast<const uint16_t*>(p.kreg) + static_cast<size_t>(h) * p.rows * D;
-    const uint16_t* vh = static_cast<const uint16_t*>(p.vreg) + static_cast<size_t>(h) * D * p.rows;
-
-    // ---- Q^T operands ----------------------------------------------------------
-    const int qrow0 = qt * Sh::QROWS + wave * QB * 32;
-    bf16x8 qf[QB][KS];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int r = qrow0 + qb * 32 + l32;
-        const bool ok = r < p.nq;
-        const size_t g = (static_cast<size_t>(frame) * p.nq + (ok ? r : 0)) * p.H + h;
-        const uint16_t* src = static_cast<const uint16_t*>(p.q) + g * D + hl * 8;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 u = ok ? *reinterpret_cast<const u32x4*>(src + ks * 16) : u32x4{0u, 0u, 0u, 0u};
-            qf[qb][ks] = __builtin_bit_cast(bf16x8, u);
+        const SegSrc<false> segs{p, PreSegs{}};
+        const int n = segs.total();
+        const int64_t hn = static_cast<int64_t>(p.H) * n;
+        int64_t f = hn * item / p.ncols;
+        const int64_t f1 = hn * (item + 1) / p.ncols;
+        bool first = true;
+        while (f < f1) {
+            const int h = static_cast<int>(f / n);
+            const int64_t h0 = static_cast<int64_t>(h) * n;
+            const int t0 = static_cast<int>(f - h0);
+            const int t1 = static_cast<int>(f1 - h0 < n ? f1 - h0 : n);
+            const int piece = (t0 == 0 && t1 == n) ? -1 : 2 * item + (first ? 0 : 1);
+            if (!first) sync_tiles<0>();                 // every wave is done with the last range's tiles
+            attend_range<D, NW, QB, false>(p, segs, h, 0, qt, t0, t1, piece, KB, VB, tid);
+            f = h0 + t1;
+            first = false;
         }
     }
+}
 
-    f32x16 o[QB][DB];
-    float m[QB], l[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        m[qb] = -INFINITY;
-        l[qb] = 0.f;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[qb][db][i] = 0.f;
+// Merge of the streaming partials: for head h the columns c_lo .. c_hi cover
+// its tiles, and column c holds its piece in slot 2c if head h is the first
+// head of the column, else in slot 2c + 1.
+//   O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c,  M = max_c m_c.
+// Heads that lie inside one column were written by the attention kernel.
+__device__ __forceinline__ int column_of(int64_t x, int64_t hn, int ncols) {
+    return static_cast<int>(((x + 1) * ncols + hn - 1) / hn) - 1;   // the c with start(c) <= x < start(c + 1)
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                                                    uint16_t* __restrict__ out, float* __restrict__ lse, int H, int nq,
+                                                    int n, int ncols) {
+    constexpr int C = D / 4;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= H * nq * C) return;
+    const int chunk = idx % C;
+    const int r = (idx / C) % nq;
+    const int h = idx / (C * nq);
+    const int64_t hn = static_cast<int64_t>(H) * n;
+    const int64_t a = static_cast<int64_t>(h) * n;
+    const int c_lo = column_of(a, hn, ncols);
+    const int c_hi = column_of(a + n - 1, hn, ncols);
+    if (c_lo == c_hi) return;
+    float M = -INFINITY;
+    for (int c = c_lo; c <= c_hi; ++c) {
+        const int piece = 2 * c + (hn * c / ncols >= a ? 0 : 1);
+        M = fmaxf(M, part_ml[(static_cast<size_t>(piece) * nq + r) * 2]);
     }
-    const float sl2 = p.scale_log2;
-
-    if (n > 0) {
-        // cursors of tiles j-1, j, j+1, j+2 (clamped to the last tile)
-        Cursor c0 = cursor_at(segs, t_begin);
-        Cursor c1 = c0;
-        if (n > 1) cursor_next(segs, &c1);
-        Cursor c2 = c1;
-        if (n > 2) cursor_next(segs, &c2);
-        Cursor cm1 = c0;
-
-        // prologue: K_0, K_1 in flight; V1 cleared (iteration 0 multiplies it by P = 0)
-        load_k_lds<D, NW>(kh, c0.base, K0, wave, lane);
-        load_k_lds<D, NW>(kh, c1.base, K1, wave, lane);
-        for (int e = tid; e < D * KT / 8; e += NT) reinterpret_cast<u32x4*>(V1)[e] = u32x4{0u, 0u, 0u, 0u};
-        __syncthreads();
-
-        f32x16 sreg[2][QB];
-        bf16x8 PA[2][QB][2], PB[2][QB][2];
-        {
-            const f32x16 zero16 = {};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const int row = kb * 32 + l32;
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(&K0[(row * CPR + ((ks * 2 + hl) ^ lds_swz<CPR>(l32))) * 8]);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-                        sreg[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, a), qf[qb][ks], ks == 0 ? zero16 : sreg[kb][qb], 0, 0, 0);
-                }
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) PB[kb][qb][hf] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-        }
-
-        int j = 0;
-        for (; j + 1 < n; j += 2) {
-            pipe_iter<D, NW, QB>(j, n, sreg, PA, PB, cm1, c0, c1, c2, segs, o, m, l, qf, K1, V1, K0, V0, kh, vh,
-                                 p.rows, sl2, tid);
-            pipe_iter<D, NW, QB>(j + 1, n, sreg, PB, PA, cm1, c0, c1, c2, segs, o, m, l, qf, K0, V0, K1, V1, kh, vh,
-                                 p.rows, sl2, tid);
-        }
-        if (j < n)     // n odd: one more even iteration
-            pipe_iter<D, NW, QB>(j, n, sreg, PA, PB, cm1, c0, c1, c2, segs, o, m, l, qf, K1, V1, K0, V0, kh, vh,
-                                 p.rows, sl2, tid);
-
-        // last tile's PV: V_{n-1} is in buffer (n-1) % 2, P_{n-1} in PA if n-1 is even
-        __syncthreads();
-        uint16_t* vl = ((n - 1) & 1) ? V1 : V0;
-        if (cm1.base < cm1.lo || cm1.base + KT > cm1.hi) {
-            tile_clear_edges<D, NT>(vl, cm1, tid);
-            __syncthreads();
-        }
-        if ((n - 1) & 1)
-            pipe_last_pv<D, QB>(PB, o, vl, l32, hl);
-        else
-            pipe_last_pv<D, QB>(PA, o, vl, l32, hl);
+    float Lsum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = c_lo; c <= c_hi; ++c) {
+        const int piece = 2 * c + (hn * c / ncols >= a ? 0 : 1);
+        const size_t row = static_cast<size_t>(piece) * nq + r;
+        const float ms = part_ml[row * 2];
+        const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+        Lsum += w * part_ml[row * 2 + 1];
+        acc += w * *reinterpret_cast<const f32x4*>(part_o + row * D + chunk * 4);
     }
-    write_out<D, QB, PREFILL>(p, o, m, l, qrow0, frame, h, split, l32, hl);
+    const float inv = 1.f / Lsum;
+    const size_t g = (static_cast<size_t>(r) * H + h) * D + chunk * 4;
+    *reinterpret_cast<u32x2*>(out + g) =
+        u32x2{pack_bf2(acc[0] * inv, acc[1] * inv), pack_bf2(acc[2] * inv, acc[3] * inv)};
+    if (lse != nullptr && chunk == 0) lse[static_cast<size_t>(h) * nq + r] = (M + log2f(Lsum)) * 0.69314718055994530942f;
 }
 
 // fp32 path: one thread per query row, exact online softmax in single
@@ -919,47 +714,6 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
             (m + log2f(l)) * 0.69314718055994530942f;
 }
 
-// Merge split partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-template <typename TO, int D>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
-                                                      const float* __restrict__ part_ml, TO* __restrict__ out,
-                                                      float* __restrict__ lse, int H, int nq, int splits) {
-    constexpr int C = D / 4;
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= nq * H * C) return;
-    const int chunk = idx % C;
-    const int hq = idx / C;
-    const int q = hq / H;
-    const int h = hq % H;
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s)
-        M = fmaxf(M, part_ml[((static_cast<size_t>(s) * H + h) * nq + q) * 2]);
-    float L = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < splits; ++s) {
-        const size_t row = (static_cast<size_t>(s) * H + h) * nq + q;
-        const float ms = part_ml[row * 2];
-        const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-        L += w * part_ml[row * 2 + 1];
-        const float4 v = *reinterpret_cast<const float4*>(part_o + row * D + chunk * 4);
-        acc.x += w * v.x;
-        acc.y += w * v.y;
-        acc.z += w * v.z;
-        acc.w += w * v.w;
-    }
-    const float inv = 1.f / L;
-    const size_t g = (static_cast<size_t>(q) * H + h) * D + chunk * 4;
-    if constexpr (sizeof(TO) == 2) {
-        const uint32_t w0 = pack_bf2(acc.x * inv, acc.y * inv);
-        const uint32_t w1 = pack_bf2(acc.z * inv, acc.w * inv);
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + g) = make_uint2(w0, w1);
-    } else {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + g) =
-            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    }
-    if (lse != nullptr && chunk == 0) lse[static_cast<size_t>(h) * nq + q] = (M + log2f(L)) * 0.69314718055994530942f;
-}
-
 #ifndef SWA_NW
 #define SWA_NW 4
 #endif
@@ -967,25 +721,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 #define SWA_QB 1
 #endif
 #ifndef SWA_OCC
-#define SWA_OCC 2
+#define SWA_OCC 3
 #endif
 constexpr int kNW = SWA_NW;       // waves per work-group
 constexpr int kQB = SWA_QB;       // 32-query blocks per wave
 constexpr int kOcc = SWA_OCC;     // waves per SIMD the register budget targets
 
-#ifndef SWA_PIPE
-#define SWA_PIPE 0
-#endif
-
 template <int D>
 hipError_t attn_bf16_dispatch(bool prefill, const AttnParams& p, int grid, hipStream_t stream) {
-    if (SWA_PIPE) {
-        if (prefill)
-            hipLaunchKernelGGL((attn_bf16_pipe_kernel<D, kNW, kQB, kOcc, true>), dim3(grid), dim3(kNW * 64), 0, stream, p);
-        else
-            hipLaunchKernelGGL((attn_bf16_pipe_kernel<D, kNW, kQB, kOcc, false>), dim3(grid), dim3(kNW * 64), 0, stream, p);
-        return hipGetLastError();
-    }
     if (prefill)
         hipLaunchKernelGGL((attn_bf16_kernel<D, kNW, kQB, kOcc, true>), dim3(grid), dim3(kNW * 64), 0, stream, p);
     else
@@ -1005,6 +748,15 @@ hipError_t attn_f32_dispatch(bool prefill, const AttnParams& p, hipStream_t stre
 
 }  // namespace
 
+int attention_blocks_per_cu(int dtype, int D) {
+    if (dtype != 0) return 1;
+    int n = 0;
+    const hipError_t e =
+        D == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, kNW, kQB, kOcc, false>, kNW * 64, 0)
+                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<32, kNW, kQB, kOcc, false>, kNW * 64, 0);
+    return (e == hipSuccess && n > 0) ? n : 1;
+}
+
 int attention_q_tile(int dtype) { return dtype == 0 ? Shape<kNW, kQB>::QROWS : 64; }
 
 hipError_t launch_attention(int dtype, int D, bool prefill, const AttnParams& p, int grid,
@@ -1014,25 +766,16 @@ hipError_t launch_attention(int dtype, int D, bool prefill, const AttnParams& p,
     return D == 64 ? attn_f32_dispatch<64>(prefill, p, stream) : attn_f32_dispatch<32>(prefill, p, stream);
 }
 
-hipError_t launch_combine(int dtype, int D, int H, int nq, int splits, const float* part_o,
-                          const float* part_ml, void* out, float* lse, hipStream_t stream) {
-    const int n = nq * H * (D / 4);
-    const dim3 grid((n + 255) / 256);
-    if (dtype == 0) {
-        if (D == 64)
-            hipLaunchKernelGGL((combine_kernel<uint16_t, 64>), grid, dim3(256), 0, stream, part_o, part_ml,
-                               static_cast<uint16_t*>(out), lse, H, nq, splits);
-        else
-            hipLaunchKernelGGL((combine_kernel<uint16_t, 32>), grid, dim3(256), 0, stream, part_o, part_ml,
-                               static_cast<uint16_t*>(out), lse, H, nq, splits);
-    } else {
-        if (D == 64)
-            hipLaunchKernelGGL((combine_kernel<float, 64>), grid, dim3(256), 0, stream, part_o, part_ml,
-                               static_cast<float*>(out), lse, H, nq, splits);
-        else
-            hipLaunchKernelGGL((combine_kernel<float, 32>), grid, dim3(256), 0, stream, part_o, part_ml,
-                               static_cast<float*>(out), lse, H, nq, splits);
-    }
+hipError_t launch_merge(int D, int H, int nq, int n, int ncols, const float* part_o, const float* part_ml, void* out,
+                        float* lse, hipStream_t stream) {
+    const int total = H * nq * (D / 4);
+    const dim3 grid((total + 255) / 256);
+    if (D == 64)
+        hipLaunchKernelGGL((merge_kernel<64>), grid, dim3(256), 0, stream, part_o, part_ml,
+                           static_cast<uint16_t*>(out), lse, H, nq, n, ncols);
+    else
+        hipLaunchKernelGGL((merge_kernel<32>), grid, dim3(256), 0, stream, part_o, part_ml,
+                           static_cast<uint16_t*>(out), lse, H, nq, n, ncols);
     return hipGetLastError();
 }
 

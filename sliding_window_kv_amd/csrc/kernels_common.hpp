@@ -14,7 +14,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxSegs = 8;      // row segments per streaming attention call
-constexpr int kMaxSplits = 32;   // KV splits of one streaming attention call
+constexpr int kMaxCols = 256;    // columns of one streaming attention call (2 partial slots each)
 
 // Storage position of a key inside the transposed V region: within every
 // aligned group of 16 keys, bits 2 and 3 of the key index are swapped, so
@@ -77,12 +77,12 @@ struct AttnParams {
     const void* vreg;        // [H][D][rows]  (V transposed)
     void* out;               // [nq_total, H, D]
     float* lse;              // [H, nq_total] or null
-    float* part_o;           // [splits][H][nq][D] (split > 1)
-    float* part_ml;          // [splits][H][nq][2]
+    float* part_o;           // [pieces][nq][D] streaming partials
+    float* part_ml;          // [pieces][nq][2] their running max (log2 domain) and sum
     int nq;                  // query rows per frame (P)
     int H;
     int rows;                // row length of the K/V regions
-    int splits;
+    int ncols;               // streaming: columns of the (head, key tile) space
     int qtiles;              // query tiles per frame
     float scale_log2;        // log2(e) / sqrt(D)
     // prefill only

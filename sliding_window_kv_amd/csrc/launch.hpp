@@ -47,13 +47,18 @@ hipError_t launch_builder(const BuilderArgs& a, hipStream_t stream);
 hipError_t launch_mask(int F, int P, int W, int S, int token_level, uint8_t* out,
                        hipStream_t stream);
 
-// Attention: bf16 on MFMA or fp32 on the vector ALUs; split > 1 writes
-// partials that launch_combine merges.
+// Attention: bf16 on MFMA or fp32 on the vector ALUs.  Streaming bf16 runs
+// p.ncols columns of p.qtiles work-groups (grid = ncols * qtiles); heads
+// split across columns leave partials for launch_merge.
 hipError_t launch_attention(int dtype, int D, bool prefill, const AttnParams& p, int grid,
                             hipStream_t stream);
 int attention_q_tile(int dtype);
+// Work-groups of the streaming attention kernel that fit on one CU at once.
+int attention_blocks_per_cu(int dtype, int D);
 
-hipError_t launch_combine(int dtype, int D, int H, int nq, int splits, const float* part_o,
-                          const float* part_ml, void* out, float* lse, hipStream_t stream);
+// Combine the streaming partials of heads split across columns (n = key
+// tiles per head) into out [nq, H, D] bf16 and lse [H, nq] (may be null).
+hipError_t launch_merge(int D, int H, int nq, int n, int ncols, const float* part_o, const float* part_ml, void* out,
+                        float* lse, hipStream_t stream);
 
 }  // namespace swa

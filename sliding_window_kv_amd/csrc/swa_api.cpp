@@ -99,8 +99,9 @@ Layout make_layout(const swa_config* c) {
     L.layer_bytes = L.k_bytes + L.v_bytes + L.meta_bytes;
     L.work_offset = L.layer_bytes * c->num_layers;
     if (c->dtype == SWA_BF16) {
-        L.part_o_floats = int64_t(swa::kMaxSplits) * L.H * L.P * L.D;
-        L.work_bytes = align_up(L.part_o_floats * 4, 256) + align_up(int64_t(swa::kMaxSplits) * L.H * L.P * 2 * 4, 256);
+        const int64_t pieces = 2 * int64_t(swa::kMaxCols);   // two partial slots per column
+        L.part_o_floats = pieces * L.P * L.D;
+        L.work_bytes = align_up(L.part_o_floats * 4, 256) + align_up(pieces * L.P * 2 * 4, 256);
     } else {
         L.part_o_floats = 0;
         L.work_bytes = 0;
@@ -146,6 +147,7 @@ struct swa_cache {
     bool dry = false;
     int splits = 0;          // 0 = automatic
     int num_cus = 256;
+    int blocks_per_cu = 1;   // resident attention work-groups per CU
     std::vector<swa::Ring> rings;
     swa::RopeArgs rope;
 
@@ -167,15 +169,20 @@ int check_layer(const swa_cache* c, int layer) {
     return SWA_OK;
 }
 
-int pick_splits(const swa_cache* c, int groups, int total_tiles) {
-    int s = c->splits;
-    if (s <= 0) {
-        const int target = 4 * c->num_cus;
-        s = (target + groups - 1) / groups;
-    }
-    s = std::min(s, swa::kMaxSplits);
-    s = std::min(s, std::max(1, total_tiles / 2));
-    return std::max(s, 1);
+// Columns of one streaming attention call (each runs as qtiles work-groups
+// over an equal share of the H * n (head, key tile) space).  Automatic: as
+// many as the GPU holds at once, so the launch is one balanced round;
+// splits = k: every head cut into k equal pieces (k = 1: no partials).
+int pick_columns(const swa_cache* c, int qtiles, int n) {
+    const int64_t hn = int64_t(c->L.H) * n;
+    int64_t cols;
+    if (c->splits > 0)
+        cols = int64_t(c->L.H) * c->splits;
+    else
+        cols = std::max(1, c->num_cus * c->blocks_per_cu / std::max(1, qtiles));
+    cols = std::min<int64_t>(cols, swa::kMaxCols);
+    cols = std::min<int64_t>(cols, hn);
+    return static_cast<int>(std::max<int64_t>(cols, 1));
 }
 
 // Enqueue the device side of one append (special-row retention first, then
@@ -235,16 +242,15 @@ int enqueue_attention(swa_cache* c, int layer, const void* q, void* out, float* 
     if (p.seg.n == 0) return fail(SWA_E_STATE, "no cached frame to attend to");
     const int qrows = swa::attention_q_tile(c->cfg.dtype);
     p.qtiles = (L.P + qrows - 1) / qrows;
-    int splits = 1;
-    if (c->cfg.dtype == SWA_BF16) splits = pick_splits(c, L.H * p.qtiles, tiles);
-    p.splits = splits;
+    p.ncols = c->cfg.dtype == SWA_BF16 ? pick_columns(c, p.qtiles, tiles) : 1;
     p.part_o = c->part_o();
     p.part_ml = c->part_ml();
-    hipError_t e = swa::launch_attention(c->cfg.dtype, L.D, false, p, L.H * splits * p.qtiles, stream);
+    hipError_t e = swa::launch_attention(c->cfg.dtype, L.D, false, p, p.ncols * p.qtiles, stream);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
-    if (splits > 1) {
-        e = swa::launch_combine(c->cfg.dtype, L.D, L.H, L.P, splits, p.part_o, p.part_ml, out, lse, stream);
-        if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+    // every head inside one column (ncols divides H): no partials to merge
+    if (c->cfg.dtype == SWA_BF16 && !(p.ncols <= L.H && L.H % p.ncols == 0)) {
+        e = swa::launch_merge(L.D, L.H, L.P, tiles, p.ncols, p.part_o, p.part_ml, out, lse, stream);
+        if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     }
     return SWA_OK;
 }
@@ -292,6 +298,7 @@ int swa_cache_create(const swa_config* cfg, void* dev_pool, size_t pool_bytes, s
         if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
             prop.multiProcessorCount > 0)
             c->num_cus = prop.multiProcessorCount;
+        c->blocks_per_cu = swa::attention_blocks_per_cu(cfg->dtype, cfg->head_dim);
     }
     *out = c;
     return SWA_OK;
@@ -322,7 +329,7 @@ int swa_cache_layout(const swa_cache* c, swa_layout* out) {
 
 int swa_cache_set_splits(swa_cache* c, int splits) {
     if (c == nullptr) return fail(SWA_E_INVAL, "null cache");
-    if (splits < 0 || splits > swa::kMaxSplits) return fail(SWA_E_INVAL, "splits must be 0..32");
+    if (splits < 0 || splits > swa::kMaxCols) return fail(SWA_E_INVAL, "splits must be 0..256");
     c->splits = splits;
     return SWA_OK;
 }
@@ -522,7 +529,7 @@ int swa_prefill_masked(const void* q, const void* k, const void* v, int F, int P
     p.nq = P;
     p.H = H;
     p.rows = rows;
-    p.splits = 1;
+    p.ncols = 1;
     p.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
     p.F = F;
     p.W = W;

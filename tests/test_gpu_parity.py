@@ -276,6 +276,28 @@ def test_stream_with_rope_matches_oracle():
 SAMPLE_ROWS = np.array([0, 1, 4, 5, 63, 64, 127, 128, 700, 1279, 1280, 1300, 1343, 1344, 1373])
 
 
+@pytest.mark.parametrize("H,splits", [(2, 0), (2, 3), (5, 0), (16, 0), (16, 1), (16, 7)])
+def test_stream_work_split_sampled(H, splits):
+    # The streaming decomposition: automatic columns over the (head, key
+    # tile) space (heads cut mid-range, merged by a second kernel), and k
+    # equal pieces per head.  The first steps have fewer tiles than columns.
+    P, D, W, S = 1374, 64, 4, 2
+    case(f"stream work split H={H} splits={splits}")
+    gc, oc = _cache(P, H, D, swa.SWA_BF16, W, S)
+    gc.set_splits(splits)
+    for t in range(8):
+        q, k, v = frame_qkv(20 + H, t, P, H, D)
+        qd, kd, vd = dev(q), dev(k), dev(v)
+        out = torch.full_like(qd, float("nan"))
+        lse = torch.empty((H, P), dtype=torch.float32, device="cuda")
+        gc.step(0, t, qd, kd, vd, True, out, lse)
+        oc.append(t, k, v, True)
+        oc.evict()
+        ro, rl = oc.attend(q[SAMPLE_ROWS])
+        assert_close_bf16(host(out)[SAMPLE_ROWS], ro, f"t={t}")
+        assert np.abs(host(lse)[:, SAMPLE_ROWS] - rl).max() <= 1e-2
+
+
 def test_stream_step_full_size_sampled():
     # Single streaming step workload: P=1374, H=16, D=64, 8 scale + 16 window
     # frames (24 x 1374 = 32,976 visible keys), in the bench's launch config.
