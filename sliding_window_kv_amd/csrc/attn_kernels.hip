@@ -13,8 +13,9 @@
 //  * A work-group of NW waves owns NW*QB*32 query rows of one frame and head.
 //    Each wave holds Q^T for QB blocks of 32 queries in registers as the B
 //    operand of v_mfma_f32_32x32x16_bf16.
-//  * Keys stream through LDS in tiles of 64 rows, double-buffered, loaded
-//    with direct global->LDS 16-byte loads (no staging registers).  K is
+//  * Keys stream through LDS in tiles of 64 rows, in a ring of kRing
+//    buffers (kRing - 1 tiles in flight while one is consumed), loaded with
+//    direct global->LDS 16-byte loads (no staging registers).  K is
 //    kept as [64][D], V^T as [D][64]; 16-byte chunks are XOR-swizzled by row
 //    so the MFMA operand reads are free of bank conflicts.
 //  * S^T = K Q^T: the accumulator layout puts one query per lane column and
@@ -43,7 +44,8 @@ constexpr int KALIGN = 16;        // tile start alignment (rows)
 #ifndef SWA_RING
 #define SWA_RING 3
 #endif
-constexpr int kRing = SWA_RING;   // K/V tile buffers of the straightforward kernel
+constexpr int kRing = SWA_RING;   // K/V tile buffers in the ring
+constexpr int kMaxBufs = 5;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -266,16 +268,20 @@ template <int D, int NW>
 __device__ __forceinline__ void tile_load(const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
                                           int base, uint16_t* ks, uint16_t* vs, int wave) {
     using TO = TileOffsets<D, NW>;
-    const uint16_t* kt = kh + static_cast<size_t>(base) * D;
-    const uint16_t* vt = vh + base;
+    // scalar base + unsigned 32-bit byte offset: the loads take the
+    // SGPR-base form and need no per-load 64-bit address arithmetic
+    const char* kt = reinterpret_cast<const char*>(kh + static_cast<size_t>(base) * D);
+    const char* vt = reinterpret_cast<const char*>(vh + base);
 #pragma unroll
     for (int i = 0; i < TO::NK; ++i)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt + off.k[i]),
-                                         (__attribute__((address_space(3))) void*)(ks + (i * NW + wave) * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(kt + static_cast<uint32_t>(off.k[i]) * 2u),
+            (__attribute__((address_space(3))) void*)(ks + (i * NW + wave) * 512), 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < TO::NV; ++i)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vt + off.v[i]),
-                                         (__attribute__((address_space(3))) void*)(vs + (i * NW + wave) * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(vt + static_cast<uint32_t>(off.v[i]) * 2u),
+            (__attribute__((address_space(3))) void*)(vs + (i * NW + wave) * 512), 16, 0, 0);
 }
 
 // The three phases of one 64-key tile for one wave.  LDS reads address a
@@ -337,11 +343,15 @@ __device__ __forceinline__ void tile_softmax(f32x16 (&s)[2][QB], const Cursor& c
     constexpr int DB = D / 32;
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
     if (cur.base < cur.lo || cur.base + KT > cur.hi) {
+        // rare path: its 32 per-lane key offsets must not be hoisted into
+        // registers held across the whole loop
+        int hx = hl;
+        asm volatile("" : "+v"(hx));
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int key = cur.base + kb * 32 + 8 * (i >> 2) + 4 * hl + (i & 3);
+                const int key = cur.base + kb * 32 + 8 * (i >> 2) + 4 * hx + (i & 3);
                 if (key < cur.lo || key >= cur.hi) {
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) s[kb][qb][i] = -INFINITY;
@@ -441,14 +451,14 @@ __device__ __forceinline__ void sync_tiles() {
 template <int D, int NW, int QB, int NB, int U, class Src>
 __device__ __forceinline__ void ring_iter(int it, int ntiles, Cursor (&cq)[NB], Cursor& ld, const Src& segs,
                                           const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
-                                          uint16_t* const (&kbuf)[4], uint16_t* const (&vbuf)[4], const bf16x8 (&qf)[QB][D / 16],
+                                          uint16_t* const (&kbuf)[kMaxBufs], uint16_t* const (&vbuf)[kMaxBufs], const bf16x8 (&qf)[QB][D / 16],
                                           f32x16 (&o)[QB][D / 32], float (&m)[QB], float (&l)[QB], float sl2,
                                           int tid) {
     using TO = TileOffsets<D, NW>;
     constexpr int PER_TILE = TO::NK + TO::NV;    // load instructions per wave per tile
     constexpr int NXT = (U + NB - 1) % NB;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS destinations stay scalar
     if (it + NB - 2 < ntiles)
         sync_tiles<(NB - 2) * PER_TILE>();
     else
@@ -471,7 +481,7 @@ __device__ __forceinline__ void ring_iter(int it, int ntiles, Cursor (&cq)[NB], 
 template <int D, int NW, int QB, int NB, int U, class Src>
 __device__ __forceinline__ void ring_tail(int it, int ntiles, Cursor (&cq)[NB], Cursor& ld, const Src& segs,
                                           const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
-                                          uint16_t* const (&kbuf)[4], uint16_t* const (&vbuf)[4], const bf16x8 (&qf)[QB][D / 16],
+                                          uint16_t* const (&kbuf)[kMaxBufs], uint16_t* const (&vbuf)[kMaxBufs], const bf16x8 (&qf)[QB][D / 16],
                                           f32x16 (&o)[QB][D / 32], float (&m)[QB], float (&l)[QB], float sl2,
                                           int tid) {
     if constexpr (U < NB) {
@@ -486,7 +496,7 @@ __device__ __forceinline__ void ring_tail(int it, int ntiles, Cursor (&cq)[NB], 
 template <int D, int NW, int QB, int NB, int U, class Src>
 __device__ __forceinline__ void ring_round(int it, int ntiles, Cursor (&cq)[NB], Cursor& ld, const Src& segs,
                                            const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
-                                           uint16_t* const (&kbuf)[4], uint16_t* const (&vbuf)[4], const bf16x8 (&qf)[QB][D / 16],
+                                           uint16_t* const (&kbuf)[kMaxBufs], uint16_t* const (&vbuf)[kMaxBufs], const bf16x8 (&qf)[QB][D / 16],
                                            f32x16 (&o)[QB][D / 32], float (&m)[QB], float (&l)[QB], float sl2,
                                            int tid) {
     if constexpr (U < NB) {
@@ -499,14 +509,14 @@ __device__ __forceinline__ void ring_round(int it, int ntiles, Cursor (&cq)[NB],
 // [t_begin, t_end) of the segment list, finished by write_out(piece).
 template <int D, int NW, int QB, bool PREFILL>
 __device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<PREFILL>& segs, int h, int frame,
-                                             int qt, int t_begin, int t_end, int piece, uint16_t* const (&KB)[4],
-                                             uint16_t* const (&VB)[4], int tid) {
+                                             int qt, int t_begin, int t_end, int piece, uint16_t* const (&KB)[kMaxBufs],
+                                             uint16_t* const (&VB)[kMaxBufs], int tid) {
     using Sh = Shape<NW, QB>;
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
     constexpr int NB = kRing;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS destinations stay scalar
     const int l32 = lane & 31;
     const int hl = lane >> 5;
     const int ntiles = t_end - t_begin;
@@ -575,18 +585,20 @@ __device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<P
 template <int D, int NW, int QB, int OCC, bool PREFILL>
 __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnParams p) {
     constexpr int NB = kRing;
-    static_assert(NB >= 2 && NB <= 4, "2 to 4 tile buffers");
+    static_assert(NB >= 2 && NB <= kMaxBufs, "2 to 5 tile buffers");
 
     __shared__ __attribute__((aligned(16))) uint16_t K0[KT * D];
     __shared__ __attribute__((aligned(16))) uint16_t K1[KT * D];
     __shared__ __attribute__((aligned(16))) uint16_t K2[NB > 2 ? KT * D : 8];
     __shared__ __attribute__((aligned(16))) uint16_t K3[NB > 3 ? KT * D : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t K4[NB > 4 ? KT * D : 8];
     __shared__ __attribute__((aligned(16))) uint16_t V0[D * KT];
     __shared__ __attribute__((aligned(16))) uint16_t V1[D * KT];
     __shared__ __attribute__((aligned(16))) uint16_t V2[NB > 2 ? D * KT : 8];
     __shared__ __attribute__((aligned(16))) uint16_t V3[NB > 3 ? D * KT : 8];
-    uint16_t* const KB[4] = {K0, K1, K2, K3};
-    uint16_t* const VB[4] = {V0, V1, V2, V3};
+    __shared__ __attribute__((aligned(16))) uint16_t V4[NB > 4 ? D * KT : 8];
+    uint16_t* const KB[kMaxBufs] = {K0, K1, K2, K3, K4};
+    uint16_t* const VB[kMaxBufs] = {V0, V1, V2, V3, V4};
 
     const int tid = threadIdx.x;
     const int L = xcd_remap(blockIdx.x, gridDim.x);
