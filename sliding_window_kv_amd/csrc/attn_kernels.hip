@@ -168,10 +168,13 @@ __device__ __forceinline__ void tile_clear_edges(uint16_t* vs, const Cursor& c, 
 // assembly with both registers read-write: the compiler's builtin for this
 // instruction returned the same register for both results.  The leading
 // s_nop covers the VALU-write -> permlane-read hazard.
+// Lane l gets x of lanes l % 32 (lo) and l % 32 + 32 (hi).  Written as asm:
+// the builtin, given one value for both operands, was folded as if the swap
+// changed nothing.  Not volatile, so the scheduler may move it.
 __device__ __forceinline__ void xhalf_swap(float x, float* lo, float* hi) {
     unsigned a = __builtin_bit_cast(unsigned, x);
     unsigned b = a;
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
     *lo = __builtin_bit_cast(float, a);
     *hi = __builtin_bit_cast(float, b);
 }
@@ -291,16 +294,16 @@ __device__ __forceinline__ void tile_load(const TileOffsets<D, NW>& off, const u
 template <int D>
 struct TileLanes {
     static constexpr int KS = D / 16;
-    int k[KS];               // K tile: row l32, chunk (2*ks + hl) ^ swizzle, in elements
-    int v[4];                // V^T tile: row l32, chunk (4*kb + 2*hf + hl) ^ swizzle
+    int k[KS];               // K tile: row l32, chunk (2*ks + hl) ^ swizzle, in bytes
+    int v[4];                // V^T tile: row l32, chunk (4*kb + 2*hf + hl) ^ swizzle, in bytes
     __device__ TileLanes(int l32, int hl) {
         constexpr int CPR = D / 8;
         const int ksw = lds_swz<CPR>(l32);
         const int vsw = lds_swz<8>(l32);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) k[ks] = (l32 * CPR + ((ks * 2 + hl) ^ ksw)) * 8;
+        for (int ks = 0; ks < KS; ++ks) k[ks] = (l32 * CPR + ((ks * 2 + hl) ^ ksw)) * 16;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) v[x] = l32 * KT + ((x * 2 + hl) ^ vsw) * 8;
+        for (int x = 0; x < 4; ++x) v[x] = (l32 * KT + ((x * 2 + hl) ^ vsw) * 8) * 2;
     }
     // Hide the values from loop-invariant code motion: added to each slot's
     // constant base at the read, not hoisted as one register per slot.
@@ -323,7 +326,7 @@ __device__ __forceinline__ void tile_scores(const uint16_t* ks, const bf16x8 (&q
     for (int ks_ = 0; ks_ < KS; ++ks_) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(ks + kb * 32 * D + tl.k[ks_]);
+            const u32x4 a = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(ks + kb * 32 * D) + tl.k[ks_]);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
                 s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[qb][ks_],
@@ -407,7 +410,8 @@ __device__ __forceinline__ void tile_pv(const uint16_t* vs, const bf16x8 (&pb)[2
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(vs + db * 32 * KT + tl.v[kb * 2 + hf]);
+                const u32x4 a =
+                    *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(vs + db * 32 * KT) + tl.v[kb * 2 + hf]);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
                     o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb[kb][qb][hf],

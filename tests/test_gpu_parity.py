@@ -276,7 +276,7 @@ def test_stream_with_rope_matches_oracle():
 SAMPLE_ROWS = np.array([0, 1, 4, 5, 63, 64, 127, 128, 700, 1279, 1280, 1300, 1343, 1344, 1373])
 
 
-@pytest.mark.parametrize("H,splits", [(2, 0), (2, 3), (5, 0), (16, 0), (16, 1), (16, 7)])
+@pytest.mark.parametrize("H,splits", [(2, 0), (2, 3), (5, 0), (12, 0), (16, 0), (16, 1), (16, 7), (24, 0)])
 def test_stream_work_split_sampled(H, splits):
     # The streaming decomposition: automatic columns over the (head, key
     # tile) space (heads cut mid-range, merged by a second kernel), and k
