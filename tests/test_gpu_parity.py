@@ -104,9 +104,10 @@ def test_prefill_mask_export_bit_exact():
 # bf16 streaming with scale frames, retained specials and non-keyframes
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("splits", [1, 3, 0])
-def test_stream_bf16_specials_nonkey(splits):
-    P, H, D, W, S, ns, R = 45, 2, 64, 3, 2, 5, 4
+@pytest.mark.parametrize("splits,S,ns", [(1, 2, 5), (3, 2, 5), (0, 2, 5), (0, 0, 5), (0, 2, 1)])
+def test_stream_bf16_specials_nonkey(splits, S, ns):
+    # S = 0 is include_scale_frames = false; ns = 1 is camera-only retention
+    P, H, D, W, R = 45, 2, 64, 3, 4
     case(f"stream bf16 P={P} W={W} S={S} ns={ns} R={R} splits={splits}")
     gc, oc = _cache(P, H, D, swa.SWA_BF16, W, S, cross=True, ns=ns, R=R)
     gc.set_splits(splits)
@@ -212,6 +213,28 @@ def test_stream_equals_prefill_bf16():
         assert np.abs(host(out) - pg[rows]).max() <= 1e-2
 
 
+def test_stream_equals_prefill_frame_blocks():
+    # num_frame_per_block > 1 scales the window (2 blocks x 3 frames = 6
+    # frames); the stream equals the masked prefill row block by row block.
+    F, P, H, D, W, nfpb, S = 11, 70, 2, 64, 2, 3, 1
+    case(f"stream==prefill bf16 F={F} P={P} W={W} nfpb={nfpb} S={S}")
+    q, k, v = chunk_qkv(13, F, P, H, D)
+    out_p = torch.empty((F * P, H, D), dtype=torch.bfloat16, device="cuda")
+    swa.prefill_t(dev(q), dev(k), dev(v), F, P, W, nfpb, S, out_p, None)
+    po, _ = prefill(q, k, v, F, P, W, nfpb, S)
+    gc, oc = _cache(P, H, D, swa.SWA_BF16, W, S, nfpb=nfpb)
+    for t in range(F):
+        rows = slice(t * P, (t + 1) * P)
+        qd, kd, vd = dev(q[rows]), dev(k[rows]), dev(v[rows])
+        out = torch.empty_like(qd)
+        gc.step(0, t, qd, kd, vd, True, out, None)
+        ro, _, pages = oc.step(t, q[rows], k[rows], v[rows], True)
+        assert gc.pages() == pages
+        assert_close_bf16(host(out), ro, f"stream t={t}")
+        assert_close_bf16(host(out), po[rows], f"stream==prefill t={t}")
+        assert_close_bf16(host(out_p)[rows], po[rows], f"prefill t={t}")
+
+
 def test_multi_layer_caches_are_independent():
     P, H, D = 33, 2, 64
     case("two layers")
@@ -237,16 +260,17 @@ def _ulp_bf16(x):
     return 2.0 ** (e - 7)
 
 
-@pytest.mark.parametrize("t", [0, 5, 1999])
-def test_rope3d_apply(t):
+@pytest.mark.parametrize("t,bands", [(0, (12, 10, 10)), (5, (12, 10, 10)), (1999, (12, 10, 10)), (7, (0, 16, 16))])
+def test_rope3d_apply(t, bands):
+    # (0, 16, 16): 2-D RoPE (no temporal band)
     P, H, D = 1374, 4, 64
-    case(f"rope3d t={t}")
+    case(f"rope3d t={t} bands={bands}")
     q, k, _ = frame_qkv(11, t, P, H, D)
     pos = frame_positions(t, 37, 37, 5)
     qd, kd = dev(q), dev(k)
-    swa.rope3d_t(qd, kd, torch.from_numpy(pos).cuda(), (12, 10, 10))
+    swa.rope3d_t(qd, kd, torch.from_numpy(pos).cuda(), bands)
     for got, x in ((host(qd), q), (host(kd), k)):
-        ref = rope3d(x, pos, 12, 10, 10)
+        ref = rope3d(x, pos, *bands)
         diff = np.abs(got - bf16_round_f64(ref))
         # one bf16 ulp of the exact value (floored at 2^-10 for values near 0,
         # where single-precision cancellation dominates)
