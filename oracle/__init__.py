@@ -2,4 +2,4 @@
 from .swa_oracle import *  # noqa: F401,F403
 from .swa_oracle import (CacheConfig, NaiveRingCache, RingError, REGION_FRAME,  # noqa: F401
                          REGION_SPECIAL, frame_visibility, masked_attention, prefill,
-                         rope3d, stream_replay, token_mask, window_frames)
+                         head_layer_norm, rope3d, stream_replay, token_mask, window_frames)

@@ -26,12 +26,15 @@ Readings where the pages are silent (each is listed in the design doc):
   cache's window counts frames; window -1 means no window; softmax scale is
   1/sqrt(D); keys are ordered by ascending frame index; a non-keyframe sees
   the cached keyframes plus itself; special rows are retained in a FIFO of at
-  most R entries; 3-D RoPE rotates interleaved pairs with a per-band ladder.
+  most R entries; 3-D RoPE rotates interleaved pairs with a per-band ladder;
+  the q and k norms are layer norms over head_dim with a per-feature weight
+  and bias (epsilon 1e-5 unless given).
 
 Parity unpinned (no printed values on the pages; pinned only by the quoted
 control flow and the readings above): non-keyframe visibility, cross-frame
-special retention and its bound R, and the 3-D RoPE layout relative to the
-reference model's own rotary module.
+special retention and its bound R, the 3-D RoPE layout relative to the
+reference model's own rotary module, and the kind of the q/k norm (the pages
+name it only).
 """
 from __future__ import annotations
 
@@ -202,6 +205,26 @@ def rope3d(x: np.ndarray, pos: np.ndarray, pairs_t: int, pairs_h: int, pairs_w: 
     out[..., 0::2] = z.real
     out[..., 1::2] = z.imag
     return out
+
+
+# ---------------------------------------------------------------------------
+# Per-head q/k normalisation
+# ---------------------------------------------------------------------------
+
+def head_layer_norm(x: np.ndarray, weight: np.ndarray, bias: np.ndarray, eps: float = 1e-5) -> np.ndarray:
+    """Normalise every (token, head) row of x [N, H, D] over head_dim.
+
+    The streaming branch's pre-attention pass names a q norm and a k norm
+    between the reshape to heads and RoPE (codehub.bot, FlashInferBlock.forward,
+    the compiled pre-attention step) but not their kind.  Read as a layer
+    norm over the D features of one head: subtract the row mean, divide by
+    sqrt(biased variance + eps), then scale by weight[d] and add bias[d]
+    (weight and bias of length D, shared by all heads and tokens).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    mean = x.mean(axis=-1, keepdims=True)
+    var = ((x - mean) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mean) / np.sqrt(var + float(eps)) * np.asarray(weight, np.float64) + np.asarray(bias, np.float64)
 
 
 # ---------------------------------------------------------------------------

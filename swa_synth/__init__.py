@@ -25,6 +25,7 @@ __all__ = [
     "frame_qkv",
     "frame_positions",
     "chunk_qkv",
+    "norm_weights",
 ]
 
 
@@ -82,3 +83,14 @@ def frame_positions(t: int, grid_h: int, grid_w: int, n_special: int) -> np.ndar
     pos[n_special:, 1] = j // grid_w
     pos[n_special:, 2] = j % grid_w
     return pos
+
+
+def norm_weights(config_id: int, D: int) -> np.ndarray:
+    """float32 [4, D]: q weight, q bias, k weight, k bias (weights near 1, biases near 0)."""
+    rng = np.random.default_rng([int(config_id), 7919])
+    w = np.empty((4, D), dtype=np.float32)
+    w[0] = 1.0 + 0.1 * rng.standard_normal(D, dtype=np.float32)
+    w[1] = 0.1 * rng.standard_normal(D, dtype=np.float32)
+    w[2] = 1.0 + 0.1 * rng.standard_normal(D, dtype=np.float32)
+    w[3] = 0.1 * rng.standard_normal(D, dtype=np.float32)
+    return w
