@@ -248,6 +248,32 @@ int swa_stream_step(swa_cache* cache, int layer, int64_t frame_t, void* q, const
                     swa_stream_t stream);
 
 /*
+ * Per-head layer norm of q and k in place, device [n_tokens, H, D].  The
+ * streaming branch's pre-attention pass ([FB]) applies a q norm and a k norm
+ * after the reshape to heads and before RoPE; their kind is not stated there
+ * and is read as a layer norm over head_dim: each (token, head) row minus
+ * its mean, divided by sqrt(biased variance + eps), times weight[d] plus
+ * bias[d].  weights: device float [4][D] = q weight, q bias, k weight,
+ * k bias (shared by all heads).  Math in float, one rounding to dtype.
+ * Either q or k may be NULL.  SWA_E_INVAL for null weights, eps < 0 or a
+ * bad shape; SWA_E_UNSUPPORTED for head_dim other than 32 or 64.
+ */
+int qk_norm_apply(void* q, void* k, int n_tokens, int H, int D, const float* weights, float eps, int dtype,
+                  swa_stream_t stream);
+
+/*
+ * swa_stream_step with the q/k norm fused into the append pass ([FB]: the
+ * pre-attention pass normalises q and k, then applies RoPE, then the frame
+ * is appended): q is normalised (and rotated when pos_thw is not NULL) in
+ * place; k is normalised (and rotated) on its way into the cache; v is
+ * copied.  weights and eps as in qk_norm_apply.  Same errors as
+ * swa_stream_step, plus SWA_E_INVAL for null weights or eps < 0.
+ */
+int swa_stream_step_normed(swa_cache* cache, int layer, int64_t frame_t, void* q, const void* k, const void* v,
+                           const float* qk_norm_weights, float eps, const int32_t* pos_thw, int keyframe,
+                           void* out, float* lse, swa_stream_t stream);
+
+/*
  * Masked prefill of F frames submitted at once ([G] "Mask Generation in
  * CausalAttention"): query frame i sees key frame j iff j <= i and
  * (j >= i - W + 1 or j < scale_frames), W = sliding_window_size *

@@ -76,6 +76,9 @@ _PROTOS = {
     "kvcache_read_device_pages": (_i32, [_vp, _i32, ctypes.POINTER(swa_page), _i32, ctypes.POINTER(_i32), _vp]),
     "rope3d_apply": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _vp]),
     "swa_stream_step": (_i32, [_vp, _i32, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
+    "swa_stream_step_normed": (_i32, [_vp, _i32, _i64, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _i32, _vp, _vp,
+                                      _vp]),
+    "qk_norm_apply": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, ctypes.c_float, _i32, _vp]),
     "swa_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "swa_prefill_masked": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                   _vp, _sz, _vp]),
@@ -183,6 +186,15 @@ def swa_stream_step(h, layer, frame_t, q, k, v, pos, keyframe, out, lse, stream=
     return check(lib().swa_stream_step(h, layer, frame_t, q, k, v, pos, int(keyframe), out, lse, stream))
 
 
+def swa_stream_step_normed(h, layer, frame_t, q, k, v, weights, eps, pos, keyframe, out, lse, stream=None):
+    return check(lib().swa_stream_step_normed(h, layer, frame_t, q, k, v, weights, eps, pos, int(keyframe), out, lse,
+                                              stream))
+
+
+def qk_norm_apply(q, k, n_tokens, H, D, weights, eps, dtype, stream=None):
+    return check(lib().qk_norm_apply(q, k, n_tokens, H, D, weights, eps, dtype, stream))
+
+
 def swa_prefill_workspace_bytes(F, P, H, D, dtype):
     return lib().swa_prefill_workspace_bytes(F, P, H, D, dtype)
 
@@ -263,6 +275,11 @@ class SwaCache:
         swa_stream_step(self.handle, layer, t, _ptr(q), _ptr(k), _ptr(v), _ptr(pos), keyframe, _ptr(out),
                         _ptr(lse), _stream())
 
+    def step_normed(self, layer, t, q, k, v, weights, eps=1e-5, keyframe=True, out=None, lse=None, pos=None):
+        """Streaming step with the per-head q/k layer norm fused into the append (weights: float [4, D])."""
+        swa_stream_step_normed(self.handle, layer, t, _ptr(q), _ptr(k), _ptr(v), _ptr(weights), eps, _ptr(pos),
+                               keyframe, _ptr(out), _ptr(lse), _stream())
+
     def append(self, layer, t, k, v, keyframe=True):
         kvcache_append(self.handle, layer, t, _ptr(k), _ptr(v), keyframe, _stream())
 
@@ -319,6 +336,14 @@ def rope3d_t(q, k, pos, pairs, theta=10000.0):
     n, H, D = (q if q is not None else k).shape
     dtype = SWA_BF16 if (q if q is not None else k).dtype == torch.bfloat16 else SWA_F32
     rope3d_apply(_ptr(q), _ptr(k), _ptr(pos), n, H, D, pairs[0], pairs[1], pairs[2], theta, dtype, _stream())
+
+
+def qk_norm_t(q, k, weights, eps=1e-5):
+    """qk_norm_apply over torch tensors [n, H, D] in place (either may be None; weights float [4, D])."""
+    import torch
+    n, H, D = (q if q is not None else k).shape
+    dtype = SWA_BF16 if (q if q is not None else k).dtype == torch.bfloat16 else SWA_F32
+    qk_norm_apply(_ptr(q), _ptr(k), n, H, D, _ptr(weights), eps, dtype, _stream())
 
 
 def prefill_mask_t(F, P, sliding_window_size, num_frame_per_block, scale_frames, token_level, out):

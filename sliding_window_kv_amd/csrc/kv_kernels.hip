@@ -64,15 +64,58 @@ __device__ __forceinline__ void rope_chunk(T* x, const RopeArgs& r, const int32_
     }
 }
 
+// Rotate E/2 pairs of one chunk of k and one of q held as floats (the
+// angles of a token computed once for both).
+template <int E>
+__device__ __forceinline__ void rope_pairs2(float* x, float* y, const RopeArgs& r, const int32_t* pos3, int p0) {
+#pragma unroll
+    for (int j = 0; j < E / 2; ++j) {
+        float c, s;
+        rope_cs(r, pos3, p0 + j, &c, &s);
+        const float a = x[2 * j], b = x[2 * j + 1];
+        x[2 * j] = a * c - b * s;
+        x[2 * j + 1] = a * s + b * c;
+        const float qa = y[2 * j], qb = y[2 * j + 1];
+        y[2 * j] = qa * c - qb * s;
+        y[2 * j + 1] = qa * s + qb * c;
+    }
+}
+
+// Layer norm of one (token, head) row over head_dim, the row held as CPR
+// consecutive lanes of E floats each: mean, then the biased variance of the
+// centred values, both reduced across the CPR lanes; then weight and bias
+// (w, b point at this lane's E features).  Every lane of the wave takes
+// part in the reductions.
+template <int CPR, int E>
+__device__ __forceinline__ void row_layer_norm(float (&x)[E], const float* w, const float* b, float eps) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) s += x[e];
+#pragma unroll
+    for (int off = 1; off < CPR; off <<= 1) s += __shfl_xor(s, off);
+    const float mean = s * (1.f / (CPR * E));
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        x[e] -= mean;
+        ss = fmaf(x[e], x[e], ss);
+    }
+#pragma unroll
+    for (int off = 1; off < CPR; off <<= 1) ss += __shfl_xor(ss, off);
+    const float inv = 1.f / sqrtf(ss * (1.f / (CPR * E)) + eps);
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = fmaf(x[e] * inv, w[e], b[e]);
+}
+
 constexpr int kTileRows = 64;
 
 // One block = 64 destination rows (16-aligned) of one head.
-template <typename T, int D, bool ROPE>
+template <typename T, int D, bool ROPE, bool NORM>
 __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                      T* __restrict__ kreg, T* __restrict__ vreg,
                                                      T* __restrict__ q, const int32_t* __restrict__ pos,
-                                                     RopeArgs rope, int H, int n_tok, int row0, int rows,
-                                                     int32_t* meta_slot, int32_t frame_id) {
+                                                     RopeArgs rope, NormArgs norm, int H, int n_tok, int row0,
+                                                     int rows, int32_t* meta_slot, int32_t frame_id) {
     constexpr int E = Elt<T>::kPer16B;
     constexpr int CPR = D / E;               // 16-byte chunks per row
     constexpr int LD = D + 2;                // padded LDS row
@@ -90,7 +133,37 @@ __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, co
         const int r = base + rr;
         const int tok = r - row0;
         Chunk<T> kv, vv;
-        if (tok >= 0 && tok < n_tok) {
+        if constexpr (NORM) {
+            // every lane takes part in the row reductions: rows outside the
+            // frame read token 0 and store nothing
+            const bool ok = tok >= 0 && tok < n_tok;
+            const int t = ok ? tok : 0;
+            const size_t src = (static_cast<size_t>(t) * H + h) * D + ch * E;
+            kv.u = *reinterpret_cast<const uint4*>(k + src);
+            vv.u = *reinterpret_cast<const uint4*>(v + src);
+            Chunk<T> qv;
+            qv.u = *reinterpret_cast<const uint4*>(q + src);
+            float kf[E], qf[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                kf[e] = Elt<T>::ld(kv.e[e]);
+                qf[e] = Elt<T>::ld(qv.e[e]);
+            }
+            row_layer_norm<CPR, E>(qf, norm.w + ch * E, norm.w + D + ch * E, norm.eps);
+            row_layer_norm<CPR, E>(kf, norm.w + 2 * D + ch * E, norm.w + 3 * D + ch * E, norm.eps);
+            if constexpr (ROPE) rope_pairs2<E>(kf, qf, rope, pos + 3 * t, ch * E / 2);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                kv.e[e] = Elt<T>::st(kf[e]);
+                qv.e[e] = Elt<T>::st(qf[e]);
+            }
+            if (ok) {
+                *reinterpret_cast<uint4*>(q + src) = qv.u;
+                *reinterpret_cast<uint4*>(kreg + (static_cast<size_t>(h) * rows + r) * D + ch * E) = kv.u;
+            } else {
+                vv.u = make_uint4(0, 0, 0, 0);
+            }
+        } else if (tok >= 0 && tok < n_tok) {
             const size_t src = (static_cast<size_t>(tok) * H + h) * D + ch * E;
             kv.u = *reinterpret_cast<const uint4*>(k + src);
             vv.u = *reinterpret_cast<const uint4*>(v + src);
@@ -182,6 +255,36 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ q, T* __restr
     }
 }
 
+// Per-head layer norm of q and k in place (either may be null); one thread
+// per 16-byte chunk, the CPR chunks of a row in consecutive lanes.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void qknorm_kernel(T* __restrict__ q, T* __restrict__ k, NormArgs norm, int64_t n) {
+    constexpr int E = Elt<T>::kPer16B;
+    constexpr int CPR = D / E;
+    // grid-stride over whole waves, so the lanes of a row stay together and
+    // every lane reaches the reductions (chunks past n compute on chunk 0)
+    for (int64_t c0 = blockIdx.x * 256ll; c0 < n; c0 += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t c = c0 + threadIdx.x;
+        const bool ok = c < n;
+        const int64_t cc = ok ? c : 0;
+        const int ch = static_cast<int>(cc % CPR);
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            T* x = which == 0 ? q : k;
+            if (x == nullptr) continue;              // uniform
+            Chunk<T> xv;
+            xv.u = *reinterpret_cast<const uint4*>(x + cc * E);
+            float f[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) f[e] = Elt<T>::ld(xv.e[e]);
+            row_layer_norm<CPR, E>(f, norm.w + 2 * which * D + ch * E, norm.w + (2 * which + 1) * D + ch * E, norm.eps);
+#pragma unroll
+            for (int e = 0; e < E; ++e) xv.e[e] = Elt<T>::st(f[e]);
+            if (ok) *reinterpret_cast<uint4*>(x + cc * E) = xv.u;
+        }
+    }
+}
+
 // Visible-page list from the device frame tables and the ring counters:
 // scale frames, retained special entries (oldest first), window frames,
 // pending non-keyframe.
@@ -243,22 +346,27 @@ __global__ __launch_bounds__(256) void mask_kernel(int F, int P, int W, int S, i
 template <typename T, int D>
 hipError_t append_dispatch(int H, int n_tok, int row0, int rows, const void* k, const void* v,
                            void* kreg, void* vreg, void* q, const int32_t* pos, const RopeArgs* rope,
-                           int32_t* meta_slot, int32_t frame_id, hipStream_t stream) {
+                           const NormArgs* norm, int32_t* meta_slot, int32_t frame_id, hipStream_t stream) {
     const int first = row0 & ~15;
     const int tiles = (row0 + n_tok - first + kTileRows - 1) / kTileRows;
     dim3 grid(tiles, H);
     RopeArgs r{};
     if (rope != nullptr) r = *rope;
-    if (rope != nullptr)
-        hipLaunchKernelGGL((append_kernel<T, D, true>), grid, dim3(256), 0, stream,
-                           static_cast<const T*>(k), static_cast<const T*>(v), static_cast<T*>(kreg),
-                           static_cast<T*>(vreg), static_cast<T*>(q), pos, r, H, n_tok, row0, rows,
-                           meta_slot, frame_id);
+    NormArgs nm{};
+    if (norm != nullptr) nm = *norm;
+#define SWA_APPEND(RO, NO)                                                                                  \
+    hipLaunchKernelGGL((append_kernel<T, D, RO, NO>), grid, dim3(256), 0, stream, static_cast<const T*>(k),  \
+                       static_cast<const T*>(v), static_cast<T*>(kreg), static_cast<T*>(vreg), static_cast<T*>(q), \
+                       pos, r, nm, H, n_tok, row0, rows, meta_slot, frame_id)
+    if (rope != nullptr && norm != nullptr)
+        SWA_APPEND(true, true);
+    else if (rope != nullptr)
+        SWA_APPEND(true, false);
+    else if (norm != nullptr)
+        SWA_APPEND(false, true);
     else
-        hipLaunchKernelGGL((append_kernel<T, D, false>), grid, dim3(256), 0, stream,
-                           static_cast<const T*>(k), static_cast<const T*>(v), static_cast<T*>(kreg),
-                           static_cast<T*>(vreg), static_cast<T*>(q), pos, r, H, n_tok, row0, rows,
-                           meta_slot, frame_id);
+        SWA_APPEND(false, false);
+#undef SWA_APPEND
     return hipGetLastError();
 }
 
@@ -266,20 +374,43 @@ hipError_t append_dispatch(int H, int n_tok, int row0, int rows, const void* k, 
 
 hipError_t launch_append(int dtype, int H, int D, int n_tok, int row0, int rows, const void* k,
                          const void* v, void* kreg, void* vreg, void* q, const int32_t* pos,
-                         const RopeArgs* rope, int32_t* meta_slot, int32_t frame_id,
+                         const RopeArgs* rope, const NormArgs* norm, int32_t* meta_slot, int32_t frame_id,
                          hipStream_t stream) {
     if (dtype == 0) {
         if (D == 64)
-            return append_dispatch<uint16_t, 64>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope,
+            return append_dispatch<uint16_t, 64>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm,
                                                  meta_slot, frame_id, stream);
-        return append_dispatch<uint16_t, 32>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope,
+        return append_dispatch<uint16_t, 32>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm,
                                              meta_slot, frame_id, stream);
     }
     if (D == 64)
-        return append_dispatch<float, 64>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope,
-                                          meta_slot, frame_id, stream);
-    return append_dispatch<float, 32>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, meta_slot,
+        return append_dispatch<float, 64>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm, meta_slot,
+                                          frame_id, stream);
+    return append_dispatch<float, 32>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm, meta_slot,
                                       frame_id, stream);
+}
+
+hipError_t launch_qknorm(int dtype, int n_tok, int H, int D, void* q, void* k, const NormArgs& norm,
+                         hipStream_t stream) {
+    const int64_t n = static_cast<int64_t>(n_tok) * H * D / (dtype == 0 ? 8 : 4);
+    const int64_t want = (n + 255) / 256;
+    const int blocks = static_cast<int>(want < 4096 ? want : 4096);
+    if (dtype == 0) {
+        if (D == 64)
+            hipLaunchKernelGGL((qknorm_kernel<uint16_t, 64>), dim3(blocks), dim3(256), 0, stream,
+                               static_cast<uint16_t*>(q), static_cast<uint16_t*>(k), norm, n);
+        else
+            hipLaunchKernelGGL((qknorm_kernel<uint16_t, 32>), dim3(blocks), dim3(256), 0, stream,
+                               static_cast<uint16_t*>(q), static_cast<uint16_t*>(k), norm, n);
+    } else {
+        if (D == 64)
+            hipLaunchKernelGGL((qknorm_kernel<float, 64>), dim3(blocks), dim3(256), 0, stream,
+                               static_cast<float*>(q), static_cast<float*>(k), norm, n);
+        else
+            hipLaunchKernelGGL((qknorm_kernel<float, 32>), dim3(blocks), dim3(256), 0, stream,
+                               static_cast<float*>(q), static_cast<float*>(k), norm, n);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_retain(int dtype, int H, int D, int rows, int src_row, int dst_row, int ns,

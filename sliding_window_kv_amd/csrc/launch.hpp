@@ -14,13 +14,25 @@ struct RopeArgs {
     double freq[64];         // per pair: theta^(-kk / d_band)
 };
 
+// Per-head layer norm parameters: w = device float [4][D] (q weight, q bias,
+// k weight, k bias).
+struct NormArgs {
+    const float* w;
+    float eps;
+};
+
 // Copy n_tok tokens of k, v ([n_tok, H, D]) into rows [row0, row0 + n_tok)
 // of the K region ([H][rows][D]) and the transposed V region ([H][D][rows]).
-// With rope != null, k is rotated on the way and q ([n_tok, H, D]) is
-// rotated in place.  meta_slot, if not null, receives frame_id.
+// With norm != null, k is layer-normed per head on the way and q
+// ([n_tok, H, D]) in place; with rope != null, k is rotated on the way and q
+// in place (after the norm).  meta_slot, if not null, receives frame_id.
 hipError_t launch_append(int dtype, int H, int D, int n_tok, int row0, int rows, const void* k,
                          const void* v, void* kreg, void* vreg, void* q, const int32_t* pos,
-                         const RopeArgs* rope, int32_t* meta_slot, int32_t frame_id,
+                         const RopeArgs* rope, const NormArgs* norm, int32_t* meta_slot, int32_t frame_id,
+                         hipStream_t stream);
+
+// Per-head layer norm of q and/or k ([n_tok, H, D]) in place.
+hipError_t launch_qknorm(int dtype, int n_tok, int H, int D, void* q, void* k, const NormArgs& norm,
                          hipStream_t stream);
 
 // Copy `ns` rows starting at src_row of every head (K and V^T) to dst_row;

@@ -188,7 +188,8 @@ int pick_columns(const swa_cache* c, int qtiles, int n) {
 // Enqueue the device side of one append (special-row retention first, then
 // the frame copy with optional RoPE).
 int enqueue_append(swa_cache* c, int layer, const swa::AppendPlan& plan, int64_t t, void* q,
-                   const void* k, const void* v, const int32_t* pos, hipStream_t stream) {
+                   const void* k, const void* v, const int32_t* pos, const swa::NormArgs* norm,
+                   hipStream_t stream) {
     const Layout& L = c->L;
     const int dt = c->cfg.dtype;
     if (plan.retain) {
@@ -201,7 +202,7 @@ int enqueue_append(swa_cache* c, int layer, const swa::AppendPlan& plan, int64_t
     }
     int32_t* slot_meta = plan.keyframe ? c->meta(layer) + plan.ord_index : c->meta(layer) + L.meta_pending;
     hipError_t e = swa::launch_append(dt, L.H, L.D, L.P, plan.slot * L.P, L.rows, k, v, c->kreg(layer),
-                                      c->vreg(layer), q, pos, pos != nullptr ? &c->rope : nullptr, slot_meta,
+                                      c->vreg(layer), q, pos, pos != nullptr ? &c->rope : nullptr, norm, slot_meta,
                                       static_cast<int32_t>(t), stream);
     if (e != hipSuccess) return hip_fail(e, "append kernel launch");
     return SWA_OK;
@@ -350,7 +351,7 @@ int kvcache_append(swa_cache* c, int layer, int64_t t, const void* k, const void
     rc = c->rings[layer].plan_append(t, keyframe != 0, &plan, &err);
     if (rc != SWA_OK) return fail(rc, err);
     if (!c->dry) {
-        rc = enqueue_append(c, layer, plan, t, nullptr, k, v, nullptr, stream);
+        rc = enqueue_append(c, layer, plan, t, nullptr, k, v, nullptr, nullptr, stream);
         if (rc != SWA_OK) return rc;
     }
     c->rings[layer].commit_append(plan, t);
@@ -466,8 +467,12 @@ int rope3d_apply(void* q, void* k, const int32_t* pos, int n_tokens, int H, int 
     return SWA_OK;
 }
 
-int swa_stream_step(swa_cache* c, int layer, int64_t t, void* q, const void* k, const void* v,
-                    const int32_t* pos, int keyframe, void* out, float* lse, swa_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int stream_step(swa_cache* c, int layer, int64_t t, void* q, const void* k, const void* v, const int32_t* pos,
+                const swa::NormArgs* norm, int keyframe, void* out, float* lse, swa_stream_t stream) {
     int rc = check_layer(c, layer);
     if (rc != SWA_OK) return rc;
     if (c->dry) return fail(SWA_E_STATE, "bookkeeping-only cache cannot attend");
@@ -479,7 +484,7 @@ int swa_stream_step(swa_cache* c, int layer, int64_t t, void* q, const void* k, 
     std::string err;
     rc = ring.plan_append(t, keyframe != 0, &plan, &err);
     if (rc != SWA_OK) return fail(rc, err);
-    rc = enqueue_append(c, layer, plan, t, q, k, v, pos, stream);
+    rc = enqueue_append(c, layer, plan, t, q, k, v, pos, norm, stream);
     if (rc != SWA_OK) return rc;
     ring.commit_append(plan, t);
     if (keyframe) ring.evict();
@@ -490,6 +495,37 @@ int swa_stream_step(swa_cache* c, int layer, int64_t t, void* q, const void* k, 
         rc = ring.rollback(&err);
         if (rc != SWA_OK) return fail(rc, err);
     }
+    return SWA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int swa_stream_step(swa_cache* c, int layer, int64_t t, void* q, const void* k, const void* v,
+                    const int32_t* pos, int keyframe, void* out, float* lse, swa_stream_t stream) {
+    return stream_step(c, layer, t, q, k, v, pos, nullptr, keyframe, out, lse, stream);
+}
+
+int swa_stream_step_normed(swa_cache* c, int layer, int64_t t, void* q, const void* k, const void* v,
+                           const float* qk_norm_weights, float eps, const int32_t* pos, int keyframe, void* out,
+                           float* lse, swa_stream_t stream) {
+    if (qk_norm_weights == nullptr) return fail(SWA_E_INVAL, "null norm weights");
+    if (!(eps >= 0.f)) return fail(SWA_E_INVAL, "norm epsilon must be >= 0");
+    const swa::NormArgs norm{qk_norm_weights, eps};
+    return stream_step(c, layer, t, q, k, v, pos, &norm, keyframe, out, lse, stream);
+}
+
+int qk_norm_apply(void* q, void* k, int n_tokens, int H, int D, const float* weights, float eps, int dtype,
+                  swa_stream_t stream) {
+    if (weights == nullptr || (q == nullptr && k == nullptr)) return fail(SWA_E_INVAL, "null pointer");
+    if (n_tokens < 0 || H < 1) return fail(SWA_E_INVAL, "bad shape");
+    if (D != 32 && D != 64) return fail(SWA_E_UNSUPPORTED, "head_dim must be 32 or 64");
+    if (dtype != SWA_BF16 && dtype != SWA_F32) return fail(SWA_E_INVAL, "bad dtype");
+    if (!(eps >= 0.f)) return fail(SWA_E_INVAL, "norm epsilon must be >= 0");
+    if (n_tokens == 0) return SWA_OK;
+    hipError_t e = swa::launch_qknorm(dtype, n_tokens, H, D, q, k, swa::NormArgs{weights, eps}, stream);
+    if (e != hipSuccess) return hip_fail(e, "norm kernel launch");
     return SWA_OK;
 }
 
@@ -517,7 +553,7 @@ int swa_prefill_masked(const void* q, const void* k, const void* v, int F, int P
     void* kreg = ws;
     void* vreg = static_cast<char*>(ws) + need / 2;
     // the F frames laid out as consecutive pages (frame f in rows [f*P, (f+1)*P))
-    hipError_t e = swa::launch_append(dtype, H, D, F * P, 0, rows, k, v, kreg, vreg, nullptr, nullptr, nullptr,
+    hipError_t e = swa::launch_append(dtype, H, D, F * P, 0, rows, k, v, kreg, vreg, nullptr, nullptr, nullptr, nullptr,
                                       nullptr, 0, stream);
     if (e != hipSuccess) return hip_fail(e, "chunk layout kernel launch");
     swa::AttnParams p{};

@@ -92,6 +92,35 @@ def test_prefill_argument_checks():
     assert e.value.code == swa.SWA_E_INVAL
 
 
+def test_qk_norm_argument_checks():
+    p = ctypes.c_void_p(256)
+    for args, code in [((p, p, 10, 2, 64, None, 1e-5, swa.SWA_BF16), swa.SWA_E_INVAL),   # no weights
+                       ((None, None, 10, 2, 64, p, 1e-5, swa.SWA_BF16), swa.SWA_E_INVAL),  # no tensors
+                       ((p, p, 10, 2, 64, p, -1.0, swa.SWA_BF16), swa.SWA_E_INVAL),        # eps < 0
+                       ((p, p, -1, 2, 64, p, 1e-5, swa.SWA_BF16), swa.SWA_E_INVAL),        # bad shape
+                       ((p, p, 10, 2, 48, p, 1e-5, swa.SWA_BF16), swa.SWA_E_UNSUPPORTED),  # head_dim 48
+                       ((p, p, 10, 2, 64, p, 1e-5, 7), swa.SWA_E_INVAL)]:                  # bad dtype
+        with pytest.raises(swa.SwaError) as e:
+            swa.qk_norm_apply(*args)
+        assert e.value.code == code
+    swa.qk_norm_apply(p, p, 0, 2, 64, p, 1e-5, swa.SWA_BF16)                               # nothing to do
+    # the fused step validates its norm arguments before touching the cache
+    c = swa.make_config(10, 2, 64, sliding_window_size=2, scale_frames=1)
+    h = swa.swa_cache_create(c, None, 0)
+    try:
+        with pytest.raises(swa.SwaError) as e:
+            swa.swa_stream_step_normed(h, 0, 0, p, p, p, None, 1e-5, None, True, p, None)
+        assert e.value.code == swa.SWA_E_INVAL
+        with pytest.raises(swa.SwaError) as e:
+            swa.swa_stream_step_normed(h, 0, 0, p, p, p, p, -1.0, None, True, p, None)
+        assert e.value.code == swa.SWA_E_INVAL
+        with pytest.raises(swa.SwaError) as e:                                              # bookkeeping-only cache
+            swa.swa_stream_step_normed(h, 0, 0, p, p, p, p, 1e-5, None, True, p, None)
+        assert e.value.code == swa.SWA_E_STATE
+    finally:
+        swa.swa_cache_destroy(h)
+
+
 def _pair(P, W, S, cross, ns, R, max_frames=50):
     ocfg = CacheConfig(P=P, sliding_window_size=W, scale_frames=S, cross_frame_special=cross,
                        special_row0=0, special_rows=ns, max_special_frames=R, max_frames=max_frames)
