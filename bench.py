@@ -15,13 +15,16 @@ frame's ring page) + evict + attention (splits merged in-kernel), through the C 
                sources have changed since those counters were taken
   cpu_baseline the float64 oracle on the host cores, a few steady steps
 
---workload prefill | rope | specials | all  prints the other workloads:
+--workload prefill | rope | specials | normed | all  prints the other workloads:
   prefill   32 frames at once (43,968 tokens), window 8, 8 scale frames
   rope      2000 frames streamed with 3-D RoPE, window 6 blocks x 4 frames,
             8 scale frames (steady state t >= 31)
   specials  1600 frames, P = 1405 (28x50 + 5), window 16, 8 scale frames,
             5 special rows of up to 1000 evicted frames retained, every
             third frame a non-keyframe (append, attend, roll back)
+  normed    the rope stream's configuration with a per-head q/k layer
+            norm fused into the RoPE + append pass, against the same steps
+            run as a separate norm kernel followed by the RoPE + append
 """
 from __future__ import annotations
 
@@ -280,6 +283,66 @@ def bench_rope(args, torch, swa):
 
 
 # ---------------------------------------------------------------------------
+# the RoPE stream with the per-head q/k norm fused into the append pass
+# ---------------------------------------------------------------------------
+
+def bench_normed(args, torch, swa):
+    import numpy as np
+    from swa_synth import frame_positions, frame_qkv, norm_weights
+    P, H, D, S = 1374, 16, 64, 8
+    sws, nfpb = 6, 4
+    W = sws * nfpb
+    t0, T = S + W - 1, S + W - 1 + max(args.steps, 1)
+    cfg = swa.make_config(P, H, D, sliding_window_size=sws, num_frame_per_block=nfpb, scale_frames=S,
+                          rope=(12, 10, 10), rope_theta=10000.0)
+    fused, split = swa.SwaCache(cfg), swa.SwaCache(cfg)
+    if args.splits is not None:
+        fused.set_splits(args.splits)
+        split.set_splits(args.splits)
+    npool = 97
+    pool = [_dev(torch, frame_qkv(6, i, P, H, D)) for i in range(npool)]
+    pos = torch.from_numpy(np.stack([frame_positions(t, 37, 37, 5) for t in range(T)])).to("cuda")
+    w = torch.from_numpy(norm_weights(6, D)).to("cuda")
+    out = torch.empty((P, H, D), dtype=torch.bfloat16, device="cuda")
+
+    def step_fused(t):
+        q, k, v = pool[t % npool]
+        fused.step_normed(0, t, q, k, v, w, 1e-5, True, out, None, pos=pos[t])
+
+    def step_split(t):
+        q, k, v = pool[t % npool]
+        swa.qk_norm_t(q, k, w, 1e-5)
+        split.step(0, t, q, k, v, True, out, None, pos=pos[t])
+
+    def norm_only(t):
+        q, k, _ = pool[t % npool]
+        swa.qk_norm_t(q, k, w, 1e-5)
+
+    for t in range(t0):
+        step_fused(t)
+        step_split(t)
+    tf = _per_step(torch, step_fused, list(range(t0, T)))
+    ts = _per_step(torch, step_split, list(range(t0, T)))
+    tn = _timed(torch, norm_only, max(args.steps, 1))
+    ms, ms_split = sum(tf) / len(tf), sum(ts) / len(ts)
+    keys = (S + W) * P
+    flops = 4.0 * D * H * P * keys
+    res = _base(args, "streaming step with fused q/k norm + 3-D RoPE + append, TFLOP/s (1374 q x 43,968 keys)",
+                flops / (ms * 1e-3) / 1e12, "TFLOP/s", ms,
+                {"workload": "normed_rope_stream", "tokens_per_frame": P, "heads": H, "head_dim": D,
+                 "window_frames": W, "scale_frames": S, "rope_pairs": [12, 10, 10], "visible_keys": keys,
+                 "norm": "per-head layer norm, eps 1e-5", "timed_steps": f"t in [{t0}, {T})"})
+    res["steps"] = len(tf)
+    res["warmup"] = t0
+    res["frames_per_s_per_layer"] = round(1000.0 / ms, 1)
+    res["separate_passes_ms_per_step"] = round(ms_split, 5)
+    res["norm_pass_ms"] = round(tn, 5)
+    res["fused_pre_attention_bytes"] = 6 * P * H * D * 2
+    res["separate_pre_attention_bytes"] = 10 * P * H * D * 2
+    return res
+
+
+# ---------------------------------------------------------------------------
 # ragged frames with retained specials and non-keyframes
 # ---------------------------------------------------------------------------
 
@@ -333,7 +396,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="stream", choices=["stream", "prefill", "rope", "specials", "all"])
+    ap.add_argument("--workload", default="stream", choices=["stream", "prefill", "rope", "specials", "normed", "all"])
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
@@ -345,8 +408,9 @@ def main():
     import sliding_window_kv_amd as swa
     swa.lib()
     torch.cuda.set_device(0)
-    order = ["stream", "prefill", "rope", "specials"] if args.workload == "all" else [args.workload]
-    fns = {"stream": bench_stream, "prefill": bench_prefill, "rope": bench_rope, "specials": bench_specials}
+    order = ["stream", "prefill", "rope", "specials", "normed"] if args.workload == "all" else [args.workload]
+    fns = {"stream": bench_stream, "prefill": bench_prefill, "rope": bench_rope, "specials": bench_specials,
+           "normed": bench_normed}
     for w in order:
         print(json.dumps(fns[w](args, torch, swa)), flush=True)
 
