@@ -28,7 +28,9 @@ Readings where the pages are silent (each is listed in the design doc):
   the cached keyframes plus itself; special rows are retained in a FIFO of at
   most R entries; 3-D RoPE rotates interleaved pairs with a per-band ladder;
   the q and k norms are layer norms over head_dim with a per-feature weight
-  and bias (epsilon 1e-5 unless given).
+  and bias (epsilon 1e-5 unless given); token-level decode keeps a rolling
+  buffer of W slots per sequence and maps query head h to kv head
+  h // (Hq // Hkv).
 
 Parity unpinned (no printed values on the pages; pinned only by the quoted
 control flow and the readings above): non-keyframe visibility, cross-frame
@@ -225,6 +227,54 @@ def head_layer_norm(x: np.ndarray, weight: np.ndarray, bias: np.ndarray, eps: fl
     mean = x.mean(axis=-1, keepdims=True)
     var = ((x - mean) ** 2).mean(axis=-1, keepdims=True)
     return (x - mean) / np.sqrt(var + float(eps)) * np.asarray(weight, np.float64) + np.asarray(bias, np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Token-level decode over a rolling buffer (grouped-query heads)
+# ---------------------------------------------------------------------------
+
+class RollingDecodeCache:
+    """Per-sequence rolling buffer of W slots (the explainer's decode cache).
+
+    The key and value of the token at position i are written to slot i mod W,
+    overwriting position i - W, which no later query can see: a query at
+    position i attends itself and the W - 1 positions before it.  With
+    grouped-query attention, query head h reads kv head h // (Hq // Hkv).
+    Plain lists of float64 arrays; the slot arithmetic is kept only to report
+    where each position lives.
+    """
+
+    def __init__(self, W: int, Hkv: int, D: int):
+        if W < 1:
+            raise ValueError("window must be >= 1")
+        self.W, self.Hkv, self.D = W, Hkv, D
+        self.slots = [None] * W            # slot -> (position, k [Hkv, D], v [Hkv, D])
+
+    def append(self, pos: int, k: np.ndarray, v: np.ndarray) -> int:
+        s = pos % self.W
+        self.slots[s] = (pos, np.asarray(k, np.float64), np.asarray(v, np.float64))
+        return s
+
+    def attend(self, pos: int, q: np.ndarray):
+        """q [Hq, D] of the token at position pos -> (out [Hq, D], lse [Hq])."""
+        q = np.asarray(q, np.float64)
+        Hq = q.shape[0]
+        G = Hq // self.Hkv
+        live = [e for e in self.slots if e is not None and pos - self.W < e[0] <= pos]
+        assert live, "the current token is always visible"
+        live.sort(key=lambda e: e[0])
+        K = np.stack([e[1] for e in live])             # [n, Hkv, D]
+        V = np.stack([e[2] for e in live])
+        out = np.empty((Hq, self.D))
+        lse = np.empty(Hq)
+        for h in range(Hq):
+            g = h // G
+            s = K[:, g, :] @ q[h] / math.sqrt(self.D)
+            m = s.max()
+            w = np.exp(s - m)
+            out[h] = w @ V[:, g, :] / w.sum()
+            lse[h] = m + math.log(w.sum())
+        return out, lse
 
 
 # ---------------------------------------------------------------------------
