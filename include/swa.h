@@ -274,6 +274,37 @@ int swa_stream_step_normed(swa_cache* cache, int layer, int64_t frame_t, void* q
                            void* out, float* lse, swa_stream_t stream);
 
 /*
+ * Token-level decode over per-sequence rolling buffers ([EX]: the key and
+ * value of the token at position i live in slot i mod W, a fixed W-slot
+ * cache; each token attends itself and the W - 1 tokens before it).  With
+ * grouped-query heads (the explainer pairs the window with grouped-query
+ * attention), query head h reads kv head h / (Hq / Hkv).  bf16 only.
+ *
+ * cache: device buffer of swa_decode_cache_bytes(B, Hkv, W, D) bytes, 256-byte
+ *   aligned, caller-owned: K [B*Hkv][rows][D] then V^T [B*Hkv][D][rows]
+ *   (rows = W rounded up plus 64 rows of tile padding; V^T keys at vt_pos
+ *   as in swa_layout).  Contents need no initialisation: slot s is read only
+ *   after a step has written it.
+ * swa_decode_step: all B sequences are at the same position pos (>= 0) and
+ *   must have been stepped through positions 0 .. pos-1 before.  Writes
+ *   k, v (device [B, Hkv, D]) into slot pos mod W, then attends q (device
+ *   [B, Hq, D]) over the min(pos+1, W) live slots.  out: device [B, Hq, D];
+ *   lse: device float [B, Hq] (natural log, scores scaled by 1/sqrt(D)) or
+ *   NULL.  work: device scratch of swa_decode_workspace_bytes(Hq, Hkv, D)
+ *   bytes, 256-byte aligned (split partials; contents need no
+ *   initialisation, no state kept between calls).
+ * Errors: SWA_E_INVAL for null pointers, sizes < 1, Hq not a multiple of
+ *   Hkv, pos < 0, too small or misaligned buffers; SWA_E_UNSUPPORTED for
+ *   head_dim other than 32 or 64 or more than 32 query heads per kv head.
+ *   The size queries return 0 for invalid arguments.
+ */
+size_t swa_decode_cache_bytes(int B, int Hkv, int W, int D);
+size_t swa_decode_workspace_bytes(int Hq, int Hkv, int D);
+int swa_decode_step(void* cache, size_t cache_bytes, int B, int Hq, int Hkv, int W, int D, int64_t pos,
+                    const void* q, const void* k, const void* v, void* out, float* lse, void* work,
+                    size_t work_bytes, swa_stream_t stream);
+
+/*
  * Masked prefill of F frames submitted at once ([G] "Mask Generation in
  * CausalAttention"): query frame i sees key frame j iff j <= i and
  * (j >= i - W + 1 or j < scale_frames), W = sliding_window_size *

@@ -79,6 +79,10 @@ _PROTOS = {
     "swa_stream_step_normed": (_i32, [_vp, _i32, _i64, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _i32, _vp, _vp,
                                       _vp]),
     "qk_norm_apply": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, ctypes.c_float, _i32, _vp]),
+    "swa_decode_cache_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "swa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "swa_decode_step": (_i32, [_vp, _sz, _i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                               _vp]),
     "swa_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "swa_prefill_masked": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                   _vp, _sz, _vp]),
@@ -193,6 +197,41 @@ def swa_stream_step_normed(h, layer, frame_t, q, k, v, weights, eps, pos, keyfra
 
 def qk_norm_apply(q, k, n_tokens, H, D, weights, eps, dtype, stream=None):
     return check(lib().qk_norm_apply(q, k, n_tokens, H, D, weights, eps, dtype, stream))
+
+
+def swa_decode_cache_bytes(B, Hkv, W, D):
+    return lib().swa_decode_cache_bytes(B, Hkv, W, D)
+
+
+def swa_decode_workspace_bytes(Hq, Hkv, D):
+    return lib().swa_decode_workspace_bytes(Hq, Hkv, D)
+
+
+def swa_decode_step(cache, cache_bytes, B, Hq, Hkv, W, D, pos, q, k, v, out, lse, work, work_bytes, stream=None):
+    return check(lib().swa_decode_step(cache, cache_bytes, B, Hq, Hkv, W, D, pos, q, k, v, out, lse, work, work_bytes,
+                                       stream))
+
+
+class DecodeCache:
+    """Rolling buffers of B sequences for token decode (device memory from torch)."""
+
+    def __init__(self, B, Hq, Hkv, W, D, device="cuda"):
+        import torch
+        self.B, self.Hq, self.Hkv, self.W, self.D = B, Hq, Hkv, W, D
+        self.nbytes = swa_decode_cache_bytes(B, Hkv, W, D)
+        self.wbytes = swa_decode_workspace_bytes(Hq, Hkv, D)
+        if self.nbytes == 0 or self.wbytes == 0:
+            raise SwaError(SWA_E_INVAL, "bad decode shape")
+        self._buf = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=device)
+        self._wbuf = torch.empty(self.wbytes + 256, dtype=torch.uint8, device=device)
+        off = (-self._buf.data_ptr()) % 256
+        self.cache = self._buf[off:off + self.nbytes]
+        woff = (-self._wbuf.data_ptr()) % 256
+        self.work = self._wbuf[woff:woff + self.wbytes]
+
+    def step(self, pos, q, k, v, out, lse=None):
+        swa_decode_step(_ptr(self.cache), self.nbytes, self.B, self.Hq, self.Hkv, self.W, self.D, pos, _ptr(q),
+                        _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(self.work), self.wbytes, _stream())
 
 
 def swa_prefill_workspace_bytes(F, P, H, D, dtype):

@@ -206,8 +206,8 @@ __device__ __forceinline__ void write_out(const AttnParams& p, const f32x16 (&o)
         if (r >= p.nq) continue;
         if (piece < 0) {
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
-            const size_t g = (static_cast<size_t>(frame) * p.nq + r) * p.H + h;
-            uint16_t* dst = static_cast<uint16_t*>(p.out) + g * D;
+            const int64_t g = (static_cast<int64_t>(frame) * p.nq + r) * p.rs + h * p.hs;
+            uint16_t* dst = static_cast<uint16_t*>(p.out) + g;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -546,8 +546,8 @@ __device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<P
     for (int qb = 0; qb < QB; ++qb) {
         const int r = qrow0 + qb * 32 + l32;
         const bool ok = r < p.nq;
-        const size_t g = (static_cast<size_t>(frame) * p.nq + (ok ? r : 0)) * p.H + h;
-        const uint16_t* src = static_cast<const uint16_t*>(p.q) + g * D + hl * 8;
+        const int64_t g = (static_cast<int64_t>(frame) * p.nq + (ok ? r : 0)) * p.rs + h * p.hs;
+        const uint16_t* src = static_cast<const uint16_t*>(p.q) + g + hl * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const u32x4 u = ok ? *reinterpret_cast<const u32x4*>(src + ks * 16) : u32x4{0u, 0u, 0u, 0u};
@@ -646,7 +646,7 @@ __device__ __forceinline__ int column_of(int64_t x, int64_t hn, int ncols) {
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                                     uint16_t* __restrict__ out, float* __restrict__ lse, int H, int nq,
-                                                    int n, int ncols) {
+                                                    int n, int ncols, int64_t rs, int64_t hs) {
     constexpr int C = D / 4;
     const int idx = blockIdx.x * 256 + threadIdx.x;
     if (idx >= H * nq * C) return;
@@ -674,7 +674,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
         acc += w * *reinterpret_cast<const f32x4*>(part_o + row * D + chunk * 4);
     }
     const float inv = 1.f / Lsum;
-    const size_t g = (static_cast<size_t>(r) * H + h) * D + chunk * 4;
+    const int64_t g = r * rs + h * hs + chunk * 4;
     *reinterpret_cast<u32x2*>(out + g) =
         u32x2{pack_bf2(acc[0] * inv, acc[1] * inv), pack_bf2(acc[2] * inv, acc[3] * inv)};
     if (lse != nullptr && chunk == 0) lse[static_cast<size_t>(h) * nq + r] = (M + log2f(Lsum)) * 0.69314718055994530942f;
@@ -691,8 +691,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
     PreSegs pre{};
     if constexpr (PREFILL) pre = prefill_segs(frame, p.W, p.S, p.fP);
     const SegSrc<PREFILL> segs{p, pre};
-    const size_t g = (static_cast<size_t>(frame) * p.nq + r) * p.H + h;
-    const float* qp = static_cast<const float*>(p.q) + g * D;
+    const int64_t g = (static_cast<int64_t>(frame) * p.nq + r) * p.rs + h * p.hs;
+    const float* qp = static_cast<const float*>(p.q) + g;
     float q[D], acc[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -721,7 +721,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
             m = mnew;
         }
     }
-    float* op = static_cast<float*>(p.out) + g * D;
+    float* op = static_cast<float*>(p.out) + g;
     const float inv = 1.f / l;
 #pragma unroll
     for (int d = 0; d < D; ++d) op[d] = acc[d] * inv;
@@ -775,6 +775,26 @@ int attention_blocks_per_cu(int dtype, int D) {
 
 int attention_q_tile(int dtype) { return dtype == 0 ? Shape<kNW, kQB>::QROWS : 64; }
 
+// Token decode: one wave per work-group; its 32 query rows are the query
+// heads of one (sequence, kv head) pair.
+int attention_decode_q_rows() { return Shape<1, 1>::QROWS; }
+
+int attention_decode_blocks_per_cu(int D) {
+    int n = 0;
+    const hipError_t e =
+        D == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, 1, 1, kOcc, false>, 64, 0)
+                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<32, 1, 1, kOcc, false>, 64, 0);
+    return (e == hipSuccess && n > 0) ? n : 1;
+}
+
+hipError_t launch_attention_decode(int D, const AttnParams& p, int grid, hipStream_t stream) {
+    if (D == 64)
+        hipLaunchKernelGGL((attn_bf16_kernel<64, 1, 1, kOcc, false>), dim3(grid), dim3(64), 0, stream, p);
+    else
+        hipLaunchKernelGGL((attn_bf16_kernel<32, 1, 1, kOcc, false>), dim3(grid), dim3(64), 0, stream, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_attention(int dtype, int D, bool prefill, const AttnParams& p, int grid,
                             hipStream_t stream) {
     if (dtype == 0) return D == 64 ? attn_bf16_dispatch<64>(prefill, p, grid, stream)
@@ -783,15 +803,15 @@ hipError_t launch_attention(int dtype, int D, bool prefill, const AttnParams& p,
 }
 
 hipError_t launch_merge(int D, int H, int nq, int n, int ncols, const float* part_o, const float* part_ml, void* out,
-                        float* lse, hipStream_t stream) {
+                        float* lse, int64_t rs, int64_t hs, hipStream_t stream) {
     const int total = H * nq * (D / 4);
     const dim3 grid((total + 255) / 256);
     if (D == 64)
         hipLaunchKernelGGL((merge_kernel<64>), grid, dim3(256), 0, stream, part_o, part_ml,
-                           static_cast<uint16_t*>(out), lse, H, nq, n, ncols);
+                           static_cast<uint16_t*>(out), lse, H, nq, n, ncols, rs, hs);
     else
         hipLaunchKernelGGL((merge_kernel<32>), grid, dim3(256), 0, stream, part_o, part_ml,
-                           static_cast<uint16_t*>(out), lse, H, nq, n, ncols);
+                           static_cast<uint16_t*>(out), lse, H, nq, n, ncols, rs, hs);
     return hipGetLastError();
 }
 

@@ -81,6 +81,9 @@ struct AttnParams {
     float* part_ml;          // [pieces][nq][2] their running max (log2 domain) and sum
     int nq;                  // query rows per frame (P)
     int H;
+    // element offset of (frame, row r, head h) in q and out:
+    // (frame * nq + r) * rs + h * hs  (frame tensors: rs = H * D, hs = D)
+    int64_t rs, hs;
     int rows;                // row length of the K/V regions
     int ncols;               // streaming: columns of the (head, key tile) space
     int qtiles;              // query tiles per frame

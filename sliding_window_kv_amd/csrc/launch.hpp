@@ -71,6 +71,18 @@ int attention_blocks_per_cu(int dtype, int D);
 // Combine the streaming partials of heads split across columns (n = key
 // tiles per head) into out [nq, H, D] bf16 and lse [H, nq] (may be null).
 hipError_t launch_merge(int D, int H, int nq, int n, int ncols, const float* part_o, const float* part_ml, void* out,
-                        float* lse, hipStream_t stream);
+                        float* lse, int64_t rs, int64_t hs, hipStream_t stream);
+
+// Token decode over rolling buffers ([H = sequences x kv heads][rows][D] and
+// V^T): the streaming attention kernel with one wave per work-group, whose
+// 32 query rows are the query heads of one kv group (p.nq <= 32).
+hipError_t launch_attention_decode(int D, const AttnParams& p, int grid, hipStream_t stream);
+int attention_decode_blocks_per_cu(int D);
+int attention_decode_q_rows();
+
+// Write each of the nh (sequence, kv head) rows of k, v ([nh][D]) into row
+// `slot` of K ([nh][rows][D]) and V^T ([nh][D][rows], at vt_pos(slot)).
+hipError_t launch_decode_append(int D, int nh, int rows, int slot, const void* k, const void* v, void* kreg,
+                                void* vreg, hipStream_t stream);
 
 }  // namespace swa

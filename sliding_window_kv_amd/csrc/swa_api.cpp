@@ -222,6 +222,8 @@ int enqueue_attention(swa_cache* c, int layer, const void* q, void* out, float* 
     p.lse = lse;
     p.nq = L.P;
     p.H = L.H;
+    p.rs = int64_t(L.H) * L.D;
+    p.hs = L.D;
     p.rows = L.rows;
     p.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(L.D)));
     p.F = 1;
@@ -250,7 +252,7 @@ int enqueue_attention(swa_cache* c, int layer, const void* q, void* out, float* 
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
     // every head inside one column (ncols divides H): no partials to merge
     if (c->cfg.dtype == SWA_BF16 && !(p.ncols <= L.H && L.H % p.ncols == 0)) {
-        e = swa::launch_merge(L.D, L.H, L.P, tiles, p.ncols, p.part_o, p.part_ml, out, lse, stream);
+        e = swa::launch_merge(L.D, L.H, L.P, tiles, p.ncols, p.part_o, p.part_ml, out, lse, p.rs, p.hs, stream);
         if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     }
     return SWA_OK;
@@ -471,6 +473,39 @@ int rope3d_apply(void* q, void* k, const int32_t* pos, int n_tokens, int H, int 
 
 namespace {
 
+constexpr int kMaxDecodeCols = 2048;         // columns of one decode call (2 partial slots each)
+
+struct DecodeLayout {
+    int64_t rows, k_bytes, total;            // K and V^T regions of the rolling buffers
+};
+
+DecodeLayout decode_layout(int B, int Hkv, int W, int D) {
+    DecodeLayout d;
+    d.rows = align_up(int64_t(W) + 64, 64);
+    d.k_bytes = align_up(int64_t(B) * Hkv * d.rows * D * 2, 256);
+    d.total = 2 * d.k_bytes;
+    return d;
+}
+
+int64_t decode_work_bytes(int G, int D) {
+    const int64_t pieces = 2 * int64_t(kMaxDecodeCols);
+    return align_up(pieces * G * D * 4, 256) + align_up(pieces * G * 2 * 4, 256);
+}
+
+// Resident decode work-groups on the current device (cached per device).
+int decode_fit(int D) {
+    static int cached[2][64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int& f = cached[D == 64 ? 1 : 0][dev];
+    if (f == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        f = cus * swa::attention_decode_blocks_per_cu(D);
+    }
+    return f;
+}
+
 int stream_step(swa_cache* c, int layer, int64_t t, void* q, const void* k, const void* v, const int32_t* pos,
                 const swa::NormArgs* norm, int keyframe, void* out, float* lse, swa_stream_t stream) {
     int rc = check_layer(c, layer);
@@ -529,6 +564,83 @@ int qk_norm_apply(void* q, void* k, int n_tokens, int H, int D, const float* wei
     return SWA_OK;
 }
 
+size_t swa_decode_cache_bytes(int B, int Hkv, int W, int D) {
+    if (B < 1 || Hkv < 1 || W < 1 || (D != 32 && D != 64)) return 0;
+    if (int64_t(W) + 128 > (1ll << 30)) return 0;
+    return static_cast<size_t>(decode_layout(B, Hkv, W, D).total);
+}
+
+size_t swa_decode_workspace_bytes(int Hq, int Hkv, int D) {
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Hq / Hkv > swa::attention_decode_q_rows() || (D != 32 && D != 64))
+        return 0;
+    return static_cast<size_t>(decode_work_bytes(Hq / Hkv, D));
+}
+
+int swa_decode_step(void* cache, size_t cache_bytes, int B, int Hq, int Hkv, int W, int D, int64_t pos,
+                    const void* q, const void* k, const void* v, void* out, float* lse, void* work,
+                    size_t work_bytes, swa_stream_t stream) {
+    if (cache == nullptr || q == nullptr || k == nullptr || v == nullptr || out == nullptr || work == nullptr)
+        return fail(SWA_E_INVAL, "null pointer");
+    if (B < 1 || Hkv < 1 || Hq < 1 || W < 1) return fail(SWA_E_INVAL, "B, Hq, Hkv and W must be >= 1");
+    if (D != 32 && D != 64) return fail(SWA_E_UNSUPPORTED, "head_dim must be 32 or 64");
+    if (Hq % Hkv != 0) return fail(SWA_E_INVAL, "Hq must be a multiple of Hkv");
+    const int G = Hq / Hkv;
+    if (G > swa::attention_decode_q_rows()) return fail(SWA_E_UNSUPPORTED, "more than 32 query heads per kv head");
+    if (pos < 0) return fail(SWA_E_INVAL, "position must be >= 0");
+    if (int64_t(W) + 128 > (1ll << 30)) return fail(SWA_E_INVAL, "window too large");
+    const DecodeLayout dl = decode_layout(B, Hkv, W, D);
+    if (cache_bytes < static_cast<size_t>(dl.total)) return fail(SWA_E_INVAL, "cache smaller than swa_decode_cache_bytes()");
+    if (work_bytes < static_cast<size_t>(decode_work_bytes(G, D)))
+        return fail(SWA_E_INVAL, "workspace smaller than swa_decode_workspace_bytes()");
+    if (reinterpret_cast<uintptr_t>(cache) % 256 != 0 || reinterpret_cast<uintptr_t>(work) % 256 != 0)
+        return fail(SWA_E_INVAL, "cache and workspace must be 256-byte aligned");
+    const int nh = B * Hkv;
+    void* kreg = cache;
+    void* vreg = static_cast<char*>(cache) + dl.k_bytes;
+    const int slot = static_cast<int>(pos % W);
+    hipError_t e = swa::launch_decode_append(D, nh, static_cast<int>(dl.rows), slot, k, v, kreg, vreg, stream);
+    if (e != hipSuccess) return hip_fail(e, "decode append kernel launch");
+
+    const int n = static_cast<int>(std::min<int64_t>(pos + 1, W));   // live slots 0..n-1
+    swa::AttnParams p{};
+    p.q = q;
+    p.kreg = kreg;
+    p.vreg = vreg;
+    p.out = out;
+    p.lse = lse;
+    p.nq = G;
+    p.H = nh;
+    p.rs = D;
+    p.hs = int64_t(G) * D;
+    p.rows = static_cast<int>(dl.rows);
+    p.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
+    p.F = 1;
+    p.seg.n = 1;
+    for (int i = 0; i < swa::kMaxSegs; ++i) {
+        p.seg.lo[i] = p.seg.hi[i] = 0;
+        p.seg.tile0[i] = 1 << 30;
+    }
+    p.seg.lo[0] = 0;
+    p.seg.hi[0] = n;
+    p.seg.tile0[0] = 0;
+    const int tiles = tiles_of(0, n);
+    p.seg.total_tiles = tiles;
+    p.qtiles = 1;
+    int64_t cols = std::min<int64_t>(decode_fit(D), kMaxDecodeCols);
+    cols = std::max<int64_t>(1, std::min<int64_t>(cols, int64_t(nh) * tiles));
+    p.ncols = static_cast<int>(cols);
+    const int64_t pieces = 2 * int64_t(kMaxDecodeCols);
+    p.part_o = static_cast<float*>(work);
+    p.part_ml = reinterpret_cast<float*>(static_cast<char*>(work) + align_up(pieces * G * D * 4, 256));
+    e = swa::launch_attention_decode(D, p, p.ncols, stream);
+    if (e != hipSuccess) return hip_fail(e, "decode attention kernel launch");
+    if (!(p.ncols <= nh && nh % p.ncols == 0)) {
+        e = swa::launch_merge(D, nh, G, tiles, p.ncols, p.part_o, p.part_ml, out, lse, p.rs, p.hs, stream);
+        if (e != hipSuccess) return hip_fail(e, "decode merge kernel launch");
+    }
+    return SWA_OK;
+}
+
 size_t swa_prefill_workspace_bytes(int F, int P, int H, int D, int dtype) {
     if (F < 1 || P < 1 || H < 1 || (D != 32 && D != 64) || (dtype != SWA_BF16 && dtype != SWA_F32)) return 0;
     const int64_t rows = align_up(int64_t(F) * P + 64, 64);
@@ -564,6 +676,8 @@ int swa_prefill_masked(const void* q, const void* k, const void* v, int F, int P
     p.lse = lse;
     p.nq = P;
     p.H = H;
+    p.rs = int64_t(H) * D;
+    p.hs = D;
     p.rows = rows;
     p.ncols = 1;
     p.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));

@@ -121,6 +121,29 @@ def test_qk_norm_argument_checks():
         swa.swa_cache_destroy(h)
 
 
+def test_decode_argument_checks():
+    p = ctypes.c_void_p(256)
+    assert swa.swa_decode_cache_bytes(1, 8, 4096, 48) == 0
+    assert swa.swa_decode_workspace_bytes(33, 1, 64) == 0          # more than 32 query heads per kv head
+    assert swa.swa_decode_workspace_bytes(6, 4, 64) == 0           # not a multiple
+    need = swa.swa_decode_cache_bytes(1, 1, 16, 64)
+    # K and V^T of 1 x 1 heads, 16 slots rounded up plus 64 rows of padding, 64 bf16 each
+    assert need == 2 * ((128 * 64 * 2 + 255) // 256 * 256)
+    work = swa.swa_decode_workspace_bytes(1, 1, 64)
+    for args, code in [((None, need, 1, 1, 1, 16, 64, 0), swa.SWA_E_INVAL),          # no cache
+                       ((p, need - 1, 1, 1, 1, 16, 64, 0), swa.SWA_E_INVAL),         # cache too small
+                       ((p, need, 1, 1, 1, 16, 64, -1), swa.SWA_E_INVAL),            # negative position
+                       ((p, need, 1, 3, 2, 16, 64, 0), swa.SWA_E_INVAL),             # Hq not a multiple of Hkv
+                       ((p, need, 1, 1, 1, 0, 64, 0), swa.SWA_E_INVAL),              # empty window
+                       ((p, need, 1, 1, 1, 16, 48, 0), swa.SWA_E_UNSUPPORTED)]:      # head_dim 48
+        with pytest.raises(swa.SwaError) as e:
+            swa.swa_decode_step(*args, p, p, p, p, None, p, work)
+        assert e.value.code == code
+    with pytest.raises(swa.SwaError) as e:                                            # workspace too small
+        swa.swa_decode_step(p, need, 1, 1, 1, 16, 64, 0, p, p, p, p, None, p, work - 1)
+    assert e.value.code == swa.SWA_E_INVAL
+
+
 def _pair(P, W, S, cross, ns, R, max_frames=50):
     ocfg = CacheConfig(P=P, sliding_window_size=W, scale_frames=S, cross_frame_special=cross,
                        special_row0=0, special_rows=ns, max_special_frames=R, max_frames=max_frames)

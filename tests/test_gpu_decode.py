@@ -1,0 +1,75 @@
+"""GPU parity of token-level rolling-buffer decode with grouped-query heads
+against the float64 oracle, through the C ABI (swa_decode_step)."""
+import numpy as np
+import pytest
+import torch
+
+import sliding_window_kv_amd as swa
+from gpu_helpers import assert_close_bf16, case, dev, host
+from oracle import RollingDecodeCache
+from swa_synth import frame_qkv
+
+pytestmark = pytest.mark.gpu
+
+
+def _token(cfg, pos, B, Hq, Hkv, D):
+    """q [B, Hq, D] and k, v [B, Hkv, D] of the token at position pos (bf16 values)."""
+    _, k, v = frame_qkv(cfg, pos, B, Hkv, D)
+    q = frame_qkv(cfg + 1000, pos, B, Hq, D)[0]
+    return q, k, v
+
+
+def _vt_pos(key):
+    return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,W,D", [(2, 8, 2, 37, 64), (3, 4, 4, 16, 64), (1, 32, 1, 50, 32), (2, 6, 3, 1, 64)])
+def test_decode_matches_oracle(B, Hq, Hkv, W, D):
+    # every position from 0 through two wraps of the buffer: warm-up
+    # (pos < W), the first overwrite and the steady state
+    case(f"decode B={B} Hq={Hq} Hkv={Hkv} W={W} D={D}")
+    dc = swa.DecodeCache(B, Hq, Hkv, W, D)
+    dc.cache.fill_(0xFF)                              # NaN bf16 everywhere: stale slots must never be read
+    oc = [RollingDecodeCache(W, Hkv, D) for _ in range(B)]
+    for pos in range(2 * W + 9):
+        q, k, v = _token(40 + D, pos, B, Hq, Hkv, D)
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        dc.step(pos, dev(q), dev(k), dev(v), out, lse)
+        ro = np.empty((B, Hq, D))
+        rl = np.empty((B, Hq))
+        for b in range(B):
+            oc[b].append(pos, k[b], v[b])
+            ro[b], rl[b] = oc[b].attend(pos, q[b])
+        assert_close_bf16(host(out), ro, f"pos={pos}")
+        assert np.abs(host(lse) - rl).max() <= 1e-2, f"lse pos={pos}"
+    # the buffers hold exactly the last W tokens' bf16 keys and values
+    rows = (W + 64 + 63) // 64 * 64
+    raw = dc.cache.view(torch.bfloat16).float().cpu().numpy()
+    kb = raw[: B * Hkv * rows * D].reshape(B * Hkv, rows, D)
+    vb = raw[dc.nbytes // 4:][: B * Hkv * D * rows].reshape(B * Hkv, D, rows)
+    last = 2 * W + 8
+    for p in range(max(0, last - W + 1), last + 1):
+        _, k, v = _token(40 + D, p, B, Hq, Hkv, D)
+        s = p % W
+        assert np.array_equal(kb[:, s, :], k.reshape(B * Hkv, D))
+        assert np.array_equal(vb[:, :, _vt_pos(s)], v.reshape(B * Hkv, D))
+
+
+def test_decode_full_window_sampled():
+    # W = 4096 slots, 32 query heads over 8 kv heads, past the first wrap
+    B, Hq, Hkv, W, D = 1, 32, 8, 4096, 64
+    case("decode W=4096 Hq=32 Hkv=8")
+    dc = swa.DecodeCache(B, Hq, Hkv, W, D)
+    oc = RollingDecodeCache(W, Hkv, D)
+    check = {0, 1, 63, 64, 4095, 4096, 4097, 4200}
+    for pos in range(4201):
+        q, k, v = _token(48, pos % 997, B, Hq, Hkv, D)
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        dc.step(pos, dev(q), dev(k), dev(v), out, lse)
+        oc.append(pos, k[0], v[0])
+        if pos in check:
+            ro, rl = oc.attend(pos, q[0])
+            assert_close_bf16(host(out)[0], ro, f"pos={pos}")
+            assert np.abs(host(lse)[0] - rl).max() <= 1e-2
