@@ -15,7 +15,7 @@ frame's ring page) + evict + attention (splits merged in-kernel), through the C 
                sources have changed since those counters were taken
   cpu_baseline the float64 oracle on the host cores, a few steady steps
 
---workload prefill | rope | specials | normed | all  prints the other workloads:
+--workload prefill | rope | specials | normed | decode | all  prints the other workloads:
   prefill   32 frames at once (43,968 tokens), window 8, 8 scale frames
   rope      2000 frames streamed with 3-D RoPE, window 6 blocks x 4 frames,
             8 scale frames (steady state t >= 31)
@@ -25,6 +25,8 @@ frame's ring page) + evict + attention (splits merged in-kernel), through the C 
   normed    the rope stream's configuration with a per-head q/k layer
             norm fused into the RoPE + append pass, against the same steps
             run as a separate norm kernel followed by the RoPE + append
+  decode    token decode, 32 query heads over 8 kv heads, a 4096-slot
+            rolling buffer per sequence, batch 16 (and batch 1), buffer full
 """
 from __future__ import annotations
 
@@ -343,6 +345,49 @@ def bench_normed(args, torch, swa):
 
 
 # ---------------------------------------------------------------------------
+# token-level decode over rolling buffers (grouped-query heads)
+# ---------------------------------------------------------------------------
+
+def bench_decode(args, torch, swa):
+    from swa_synth import frame_qkv
+    Hq, Hkv, W, D = 32, 8, 4096, 64
+    res = None
+    for B in (16, 1):
+        dc = swa.DecodeCache(B, Hq, Hkv, W, D)
+        npool = 61
+        pool = []
+        for i in range(npool):
+            _, k, v = frame_qkv(7, i, B, Hkv, D)
+            q = frame_qkv(1007, i, B, Hq, D)[0]
+            pool.append(_dev(torch, (q, k, v)))
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+
+        def step(pos):
+            q, k, v = pool[pos % npool]
+            dc.step(pos, q, k, v, out)
+
+        for pos in range(W + args.warmup):           # fill the buffer, then warm up
+            step(pos)
+        t0 = W + args.warmup
+        ms = _timed(torch, lambda i: step(t0 + i), args.steps)
+        kv_bytes = 2 * B * Hkv * W * D * 2
+        io_bytes = (2 * B * Hq * D + 2 * B * Hkv * D) * 2
+        gbs = (kv_bytes + io_bytes) / (ms * 1e-3) / 1e9
+        if res is None:
+            res = _base(args, "token decode over a 4096-slot rolling buffer, GB/s of HBM (K, V, q, out)",
+                        gbs, "GB/s", ms,
+                        {"workload": "decode_gqa", "batch": B, "q_heads": Hq, "kv_heads": Hkv, "window": W,
+                         "head_dim": D, "timed_positions": f"{t0} .. {t0 + args.steps - 1} (buffer full)"})
+            res["tokens_per_s"] = round(B / (ms * 1e-3), 1)
+            res["hbm_frac"] = round(gbs / 8000.0, 4)
+            res["bytes_per_step"] = kv_bytes + io_bytes
+        else:
+            res["batch1_ms_per_step"] = round(ms, 5)
+            res["batch1_GBps"] = round(gbs, 1)
+    return res
+
+
+# ---------------------------------------------------------------------------
 # ragged frames with retained specials and non-keyframes
 # ---------------------------------------------------------------------------
 
@@ -396,7 +441,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="stream", choices=["stream", "prefill", "rope", "specials", "normed", "all"])
+    ap.add_argument("--workload", default="stream", choices=["stream", "prefill", "rope", "specials", "normed", "decode", "all"])
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
@@ -408,9 +453,9 @@ def main():
     import sliding_window_kv_amd as swa
     swa.lib()
     torch.cuda.set_device(0)
-    order = ["stream", "prefill", "rope", "specials", "normed"] if args.workload == "all" else [args.workload]
+    order = ["stream", "prefill", "rope", "specials", "normed", "decode"] if args.workload == "all" else [args.workload]
     fns = {"stream": bench_stream, "prefill": bench_prefill, "rope": bench_rope, "specials": bench_specials,
-           "normed": bench_normed}
+           "normed": bench_normed, "decode": bench_decode}
     for w in order:
         print(json.dumps(fns[w](args, torch, swa)), flush=True)
 

@@ -680,6 +680,99 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     if (lse != nullptr && chunk == 0) lse[static_cast<size_t>(h) * nq + r] = (M + log2f(Lsum)) * 0.69314718055994530942f;
 }
 
+// Merge for few query rows and many pieces per head (token decode): one
+// work-group per head.  Per row, one wave reduces the pieces' maxima and
+// sums across its lanes and leaves the normalised weights in LDS; then the
+// threads split the (row, 4-feature chunk) items and, when there are fewer
+// items than threads, the pieces too, reducing through LDS.
+constexpr int kWideWeights = 8192;          // nq * pieces per head held in LDS
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void merge_wide_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                                                         uint16_t* __restrict__ out, float* __restrict__ lse, int H,
+                                                         int nq, int n, int ncols, int64_t rs, int64_t hs) {
+    constexpr int C = D / 4;
+    __shared__ float wts[kWideWeights];
+    __shared__ f32x4 red[256];
+    const int h = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t hn = static_cast<int64_t>(H) * n;
+    const int64_t a = static_cast<int64_t>(h) * n;
+    const int c_lo = column_of(a, hn, ncols);
+    const int c_hi = column_of(a + n - 1, hn, ncols);
+    if (c_lo == c_hi) return;                       // whole head in one column: written by the attention kernel
+    const int npc = c_hi - c_lo + 1;
+    auto piece_of = [&](int j) {
+        const int c = c_lo + j;
+        return 2 * c + (hn * c / ncols >= a ? 0 : 1);
+    };
+    for (int r = wave; r < nq; r += 4) {
+        float M = -INFINITY;
+        for (int j = lane; j < npc; j += 64)
+            M = fmaxf(M, part_ml[(static_cast<size_t>(piece_of(j)) * nq + r) * 2]);
+        M = wave_max(M);
+        float Ls = 0.f;
+        for (int j = lane; j < npc; j += 64) {
+            const size_t row = static_cast<size_t>(piece_of(j)) * nq + r;
+            const float ms = part_ml[row * 2];
+            const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+            Ls += w * part_ml[row * 2 + 1];
+            wts[r * npc + j] = w;
+        }
+        Ls = wave_sum(Ls);
+        const float inv = 1.f / Ls;
+        for (int j = lane; j < npc; j += 64) wts[r * npc + j] *= inv;
+        if (lse != nullptr && lane == 0)
+            lse[static_cast<size_t>(h) * nq + r] = (M + log2f(Ls)) * 0.69314718055994530942f;
+    }
+    __syncthreads();
+    const int items = nq * C;
+    int PG = 1;                                     // piece groups per item (power of 2)
+    while (PG * 2 * items <= 256) PG *= 2;
+    for (int i0 = 0; i0 < items; i0 += 256 / PG) {
+        const int item = i0 + tid % (256 / PG);
+        const int pg = tid / (256 / PG);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const bool ok = item < items;
+        if (ok) {
+            const int r = item / C;
+            const int chunk = item % C;
+            for (int j = pg; j < npc; j += PG) {
+                const size_t row = static_cast<size_t>(piece_of(j)) * nq + r;
+                acc += wts[r * npc + j] * *reinterpret_cast<const f32x4*>(part_o + row * D + chunk * 4);
+            }
+        }
+        if (PG > 1) {
+            red[tid] = acc;
+            __syncthreads();
+            if (pg == 0) {
+                for (int g = 1; g < PG; ++g) acc += red[tid + g * (256 / PG)];
+            }
+            __syncthreads();
+        }
+        if (ok && pg == 0) {
+            const int r = item / C;
+            const int chunk = item % C;
+            const int64_t g = r * rs + h * hs + chunk * 4;
+            *reinterpret_cast<u32x2*>(out + g) = u32x2{pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3])};
+        }
+    }
+}
+
 // fp32 path: one thread per query row, exact online softmax in single
 // precision on the vector ALUs (latency-bound tiny workloads).
 template <int D, bool PREFILL>
@@ -804,6 +897,16 @@ hipError_t launch_attention(int dtype, int D, bool prefill, const AttnParams& p,
 
 hipError_t launch_merge(int D, int H, int nq, int n, int ncols, const float* part_o, const float* part_ml, void* out,
                         float* lse, int64_t rs, int64_t hs, hipStream_t stream) {
+    // pieces per head are at most ncols / H + 2
+    if (nq <= 32 && static_cast<int64_t>(nq) * (ncols / H + 2) <= kWideWeights) {
+        if (D == 64)
+            hipLaunchKernelGGL((merge_wide_kernel<64>), dim3(H), dim3(256), 0, stream, part_o, part_ml,
+                               static_cast<uint16_t*>(out), lse, H, nq, n, ncols, rs, hs);
+        else
+            hipLaunchKernelGGL((merge_wide_kernel<32>), dim3(H), dim3(256), 0, stream, part_o, part_ml,
+                               static_cast<uint16_t*>(out), lse, H, nq, n, ncols, rs, hs);
+        return hipGetLastError();
+    }
     const int total = H * nq * (D / 4);
     const dim3 grid((total + 255) / 256);
     if (D == 64)
