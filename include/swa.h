@@ -31,7 +31,8 @@
  *    null stream).  Ring bookkeeping is done on the host at enqueue time, so
  *    state errors are reported without reading the device.
  *  - A cache handle is not thread-safe.  Batch size is 1 per call.
- *  - No entry point allocates device memory.
+ *  - No entry point allocates device memory (swa_graph_create aside: the
+ *    HIP runtime allocates its own resources for a captured graph).
  */
 #ifndef SWA_H
 #define SWA_H
@@ -129,7 +130,8 @@ typedef struct swa_page {
  * Page slot s holds a frame in rows [s*P, (s+1)*P); special-ring entry e
  * holds its rows at special_row_base + e*special_rows.
  * The work area [work_offset, work_offset + work_bytes) holds the partial
- * results of streaming attention calls; it is scratch between calls.
+ * results of streaming attention calls and the step plan of captured steps;
+ * it is scratch between calls.
  */
 typedef struct swa_layout {
     int64_t layer_bytes;
@@ -272,6 +274,50 @@ int qk_norm_apply(void* q, void* k, int n_tokens, int H, int D, const float* wei
 int swa_stream_step_normed(swa_cache* cache, int layer, int64_t frame_t, void* q, const void* k, const void* v,
                            const float* qk_norm_weights, float eps, const int32_t* pos_thw, int keyframe,
                            void* out, float* lse, swa_stream_t stream);
+
+/*
+ * One streaming step of every layer as one captured HIP graph.  The
+ * streaming branch of [FB] runs, per layer, the pre-attention pass as one
+ * captured graph and then append, evict and attention; here the whole step
+ * of all num_layers layers is captured once and replayed for every frame.
+ * Every value that changes from frame to frame -- the append destination,
+ * the displaced frame's special-row copy, the frame id and the visible key
+ * segments -- is read by the kernels from a step plan in device memory (in
+ * the cache's work area), which swa_graph_step stores before each replay.
+ *
+ * swa_graph_create: bf16 caches only.  q, k, v, out: host arrays of
+ *   num_layers device pointers, each [P, H, D], fixed for the graph's
+ *   lifetime (the caller writes each frame's q, k, v there before its step;
+ *   q is normalised and rotated in place as in swa_stream_step_normed).
+ *   lse: NULL, or a host array of num_layers device float [H, P] pointers
+ *   (entries may be NULL).  pos: NULL (no RoPE) or one device int32 [P, 3]
+ *   buffer shared by the layers, rewritten by the caller per frame.
+ *   qk_norm_weights: NULL (no norm) or a host array of num_layers device
+ *   float [4][D] pointers; eps as in qk_norm_apply.  Every layer must be in
+ *   the same ring state with no non-keyframe pending.  Capturing and
+ *   instantiating the graph lets the HIP runtime allocate its own
+ *   resources; swa_graph_step allocates nothing.
+ *   Errors: SWA_E_INVAL (null pointers, eps < 0, positions without rope
+ *   bands), SWA_E_STATE (bookkeeping-only cache, layers in different
+ *   states, a pending non-keyframe), SWA_E_UNSUPPORTED (F32 cache),
+ *   SWA_E_HIP.
+ * swa_graph_step: the step of frame_t for every layer, with the semantics
+ *   of swa_stream_step (keyframe: append, evict, attend; non-keyframe:
+ *   append with eviction deferred, attend, roll back).  Enqueues one small
+ *   plan-store kernel and the graph on `stream`.  Steps of one cache must
+ *   be ordered on one stream (the plan is shared).  The host ring
+ *   bookkeeping of every layer advances as with per-layer calls, so the
+ *   per-layer entry points and page lists stay valid; after a per-layer
+ *   call leaves the layers in different states, SWA_E_STATE.
+ * swa_graph_destroy: releases the graph (not the cache, which must outlive
+ *   it).
+ */
+typedef struct swa_graph swa_graph;
+int swa_graph_create(swa_cache* cache, void* const* q, const void* const* k, const void* const* v,
+                     void* const* out, float* const* lse, const int32_t* pos_thw,
+                     const float* const* qk_norm_weights, float eps, swa_graph** graph);
+int swa_graph_step(swa_graph* graph, int64_t frame_t, int keyframe, swa_stream_t stream);
+int swa_graph_destroy(swa_graph* graph);
 
 /*
  * Token-level decode over per-sequence rolling buffers ([EX]: the key and

@@ -87,6 +87,9 @@ _PROTOS = {
     "swa_prefill_masked": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                   _vp, _sz, _vp]),
     "swa_prefill_mask": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "swa_graph_create": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.POINTER(_vp)]),
+    "swa_graph_step": (_i32, [_vp, _i64, _i32, _vp]),
+    "swa_graph_destroy": (_i32, [_vp]),
     "swa_last_error": (ctypes.c_char_p, []),
 }
 
@@ -246,6 +249,31 @@ def swa_prefill_mask(F, P, sws, nfpb, S, token_level, dev_out, stream=None):
     return check(lib().swa_prefill_mask(F, P, sws, nfpb, S, token_level, dev_out, stream))
 
 
+def _ptr_array(ptrs):
+    """A C array of device addresses (None entries become NULL), or None for None."""
+    if ptrs is None:
+        return None
+    return (_vp * len(ptrs))(*[None if x is None else x for x in ptrs])
+
+
+def swa_graph_create(h, q, k, v, out, lse, pos, norm_weights, eps):
+    """q, k, v, out: lists of device addresses (one per layer); lse, norm_weights: such lists or None."""
+    g = _vp()
+    arrs = [_ptr_array(x) for x in (q, k, v, out, lse)]
+    check(lib().swa_graph_create(h, *[ctypes.cast(a, _vp) if a is not None else None for a in arrs], pos,
+                                 ctypes.cast(_ptr_array(norm_weights), _vp) if norm_weights is not None else None,
+                                 eps, ctypes.byref(g)))
+    return g
+
+
+def swa_graph_step(g, frame_t, keyframe, stream=None):
+    return check(lib().swa_graph_step(g, frame_t, int(keyframe), stream))
+
+
+def swa_graph_destroy(g):
+    return check(lib().swa_graph_destroy(g))
+
+
 def swa_last_error():
     return lib().swa_last_error().decode()
 
@@ -354,6 +382,36 @@ class SwaCache:
         k = self.pool_view[base + L.k_offset: base + L.k_offset + nb].view(dt).view(H, rows, D)
         v = self.pool_view[base + L.v_offset: base + L.v_offset + nb].view(dt).view(H, D, rows)
         return k, v
+
+
+class SwaGraph:
+    """One captured streaming step of every layer of a SwaCache over fixed torch buffers.
+
+    q, k, v, out: lists of num_layers tensors [P, H, D]; lse: list of float [H, P] tensors (or None
+    entries) or None; pos: int32 [P, 3] tensor or None; norm_weights: list of float [4, D] tensors or
+    None.  Write each frame's inputs into the buffers, then call step(t, keyframe).
+    """
+
+    def __init__(self, cache, q, k, v, out, lse=None, pos=None, norm_weights=None, eps=1e-5):
+        self.cache = cache
+        self._keep = (q, k, v, out, lse, pos, norm_weights)
+        addr = lambda ts: None if ts is None else [None if t is None else t.data_ptr() for t in ts]
+        self.handle = swa_graph_create(cache.handle, addr(q), addr(k), addr(v), addr(out), addr(lse), _ptr(pos),
+                                       addr(norm_weights), eps)
+
+    def step(self, t, keyframe=True):
+        swa_graph_step(self.handle, t, keyframe, _stream())
+
+    def close(self):
+        if self.handle is not None:
+            swa_graph_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def prefill_t(q, k, v, F, P, sliding_window_size, num_frame_per_block, scale_frames, out, lse=None,

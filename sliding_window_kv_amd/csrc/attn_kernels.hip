@@ -82,17 +82,22 @@ __device__ __forceinline__ PreSegs prefill_segs(int i, int W, int S, int fP) {
     return s;
 }
 
-// Segment accessors: streaming reads the list from kernel arguments,
-// prefill from the scalars above.
-template <bool PREFILL>
+// Segment accessors: streaming reads the list from kernel arguments (IND:
+// from device memory, through the constant address space so the reads stay
+// uniform scalar loads; the list does not change during a launch), prefill
+// from the scalars above.
+template <bool PREFILL, bool IND = false>
 struct SegSrc {
+    using CSeg = const __attribute__((address_space(4))) SegList;
     const AttnParams& p;
     PreSegs pre;
-    __device__ int n() const { return PREFILL ? pre.n : p.seg.n; }
-    __device__ int total() const { return PREFILL ? pre.total : p.seg.total_tiles; }
-    __device__ int lo(int j) const { return PREFILL ? (j == 0 ? pre.lo0 : pre.lo1) : p.seg.lo[j]; }
-    __device__ int hi(int j) const { return PREFILL ? (j == 0 ? pre.hi0 : pre.hi1) : p.seg.hi[j]; }
-    __device__ int tile0(int j) const { return PREFILL ? (j == 0 ? 0 : pre.t1) : p.seg.tile0[j]; }
+    __device__ const SegList& ks() const { return p.seg; }
+    __device__ CSeg* ds() const { return (CSeg*)(p.dseg); }
+    __device__ int n() const { return PREFILL ? pre.n : IND ? ds()->n : ks().n; }
+    __device__ int total() const { return PREFILL ? pre.total : IND ? ds()->total_tiles : ks().total_tiles; }
+    __device__ int lo(int j) const { return PREFILL ? (j == 0 ? pre.lo0 : pre.lo1) : IND ? ds()->lo[j] : ks().lo[j]; }
+    __device__ int hi(int j) const { return PREFILL ? (j == 0 ? pre.hi0 : pre.hi1) : IND ? ds()->hi[j] : ks().hi[j]; }
+    __device__ int tile0(int j) const { return PREFILL ? (j == 0 ? 0 : pre.t1) : IND ? ds()->tile0[j] : ks().tile0[j]; }
 };
 
 // Position of tile t inside the segment list.
@@ -511,8 +516,8 @@ __device__ __forceinline__ void ring_round(int it, int ntiles, Cursor (&cq)[NB],
 
 // One work item: query tile `qt` of (frame, head h) against key tiles
 // [t_begin, t_end) of the segment list, finished by write_out(piece).
-template <int D, int NW, int QB, bool PREFILL>
-__device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<PREFILL>& segs, int h, int frame,
+template <int D, int NW, int QB, bool PREFILL, bool IND = false>
+__device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<PREFILL, IND>& segs, int h, int frame,
                                              int qt, int t_begin, int t_end, int piece, uint16_t* const (&KB)[kMaxBufs],
                                              uint16_t* const (&VB)[kMaxBufs], int tid) {
     using Sh = Shape<NW, QB>;
@@ -585,8 +590,10 @@ __device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<P
 // to the work area as partials (slot 2c for the column's first head, 2c + 1
 // for its last) and the merge kernel combines them.  With ncols near
 // (work-groups the GPU holds) / qtiles, every work-group gets the same
-// number of tiles and the launch finishes in one round.
-template <int D, int NW, int QB, int OCC, bool PREFILL>
+// number of tiles and the launch finishes in one round.  IND (captured
+// steps): the segments come from device memory and the launch has a fixed
+// number of columns, of which the first min(ncols, H * n) work.
+template <int D, int NW, int QB, int OCC, bool PREFILL, bool IND = false>
 __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnParams p) {
     constexpr int NB = kRing;
     static_assert(NB >= 2 && NB <= kMaxBufs, "2 to 5 tile buffers");
@@ -614,11 +621,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnParams p) {
         const SegSrc<true> segs{p, prefill_segs(frame, p.W, p.S, p.fP)};
         attend_range<D, NW, QB, true>(p, segs, h, frame, qt, 0, segs.total(), -1, KB, VB, tid);
     } else {
-        const SegSrc<false> segs{p, PreSegs{}};
+        const SegSrc<false, IND> segs{p, PreSegs{}};
         const int n = segs.total();
         const int64_t hn = static_cast<int64_t>(p.H) * n;
-        int64_t f = hn * item / p.ncols;
-        const int64_t f1 = hn * (item + 1) / p.ncols;
+        const int ncols = IND ? static_cast<int>(hn < p.ncols ? hn : p.ncols) : p.ncols;
+        if (IND && item >= ncols) return;            // the whole work-group: no barrier is left waiting
+        int64_t f = hn * item / ncols;
+        const int64_t f1 = hn * (item + 1) / ncols;
         bool first = true;
         while (f < f1) {
             const int h = static_cast<int>(f / n);
@@ -627,7 +636,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnParams p) {
             const int t1 = static_cast<int>(f1 - h0 < n ? f1 - h0 : n);
             const int piece = (t0 == 0 && t1 == n) ? -1 : 2 * item + (first ? 0 : 1);
             if (!first) sync_tiles<0>();                 // every wave is done with the last range's tiles
-            attend_range<D, NW, QB, false>(p, segs, h, 0, qt, t0, t1, piece, KB, VB, tid);
+            attend_range<D, NW, QB, false, IND>(p, segs, h, 0, qt, t0, t1, piece, KB, VB, tid);
             f = h0 + t1;
             first = false;
         }
@@ -646,8 +655,13 @@ __device__ __forceinline__ int column_of(int64_t x, int64_t hn, int ncols) {
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                                     uint16_t* __restrict__ out, float* __restrict__ lse, int H, int nq,
-                                                    int n, int ncols, int64_t rs, int64_t hs) {
+                                                    int n, int ncols, int64_t rs, int64_t hs,
+                                                    const int* __restrict__ dn) {
     constexpr int C = D / 4;
+    if (dn != nullptr) {                             // captured step: tile count from device memory
+        n = *dn;
+        ncols = static_cast<int64_t>(H) * n < ncols ? H * n : ncols;
+    }
     const int idx = blockIdx.x * 256 + threadIdx.x;
     if (idx >= H * nq * C) return;
     const int chunk = idx % C;
@@ -702,8 +716,13 @@ __device__ __forceinline__ float wave_sum(float x) {
 template <int D>
 __global__ __launch_bounds__(256) void merge_wide_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                                          uint16_t* __restrict__ out, float* __restrict__ lse, int H,
-                                                         int nq, int n, int ncols, int64_t rs, int64_t hs) {
+                                                         int nq, int n, int ncols, int64_t rs, int64_t hs,
+                                                         const int* __restrict__ dn) {
     constexpr int C = D / 4;
+    if (dn != nullptr) {                             // captured step: tile count from device memory
+        n = *dn;
+        ncols = static_cast<int64_t>(H) * n < ncols ? H * n : ncols;
+    }
     __shared__ float wts[kWideWeights];
     __shared__ f32x4 red[256];
     const int h = blockIdx.x;
@@ -838,7 +857,9 @@ constexpr int kOcc = SWA_OCC;     // waves per SIMD the register budget targets
 
 template <int D>
 hipError_t attn_bf16_dispatch(bool prefill, const AttnParams& p, int grid, hipStream_t stream) {
-    if (prefill)
+    if (!prefill && p.dseg != nullptr)
+        hipLaunchKernelGGL((attn_bf16_kernel<D, kNW, kQB, kOcc, false, true>), dim3(grid), dim3(kNW * 64), 0, stream, p);
+    else if (prefill)
         hipLaunchKernelGGL((attn_bf16_kernel<D, kNW, kQB, kOcc, true>), dim3(grid), dim3(kNW * 64), 0, stream, p);
     else
         hipLaunchKernelGGL((attn_bf16_kernel<D, kNW, kQB, kOcc, false>), dim3(grid), dim3(kNW * 64), 0, stream, p);
@@ -896,25 +917,25 @@ hipError_t launch_attention(int dtype, int D, bool prefill, const AttnParams& p,
 }
 
 hipError_t launch_merge(int D, int H, int nq, int n, int ncols, const float* part_o, const float* part_ml, void* out,
-                        float* lse, int64_t rs, int64_t hs, hipStream_t stream) {
+                        float* lse, int64_t rs, int64_t hs, const int* dn, hipStream_t stream) {
     // pieces per head are at most ncols / H + 2
     if (nq <= 32 && static_cast<int64_t>(nq) * (ncols / H + 2) <= kWideWeights) {
         if (D == 64)
             hipLaunchKernelGGL((merge_wide_kernel<64>), dim3(H), dim3(256), 0, stream, part_o, part_ml,
-                               static_cast<uint16_t*>(out), lse, H, nq, n, ncols, rs, hs);
+                               static_cast<uint16_t*>(out), lse, H, nq, n, ncols, rs, hs, dn);
         else
             hipLaunchKernelGGL((merge_wide_kernel<32>), dim3(H), dim3(256), 0, stream, part_o, part_ml,
-                               static_cast<uint16_t*>(out), lse, H, nq, n, ncols, rs, hs);
+                               static_cast<uint16_t*>(out), lse, H, nq, n, ncols, rs, hs, dn);
         return hipGetLastError();
     }
     const int total = H * nq * (D / 4);
     const dim3 grid((total + 255) / 256);
     if (D == 64)
         hipLaunchKernelGGL((merge_kernel<64>), grid, dim3(256), 0, stream, part_o, part_ml,
-                           static_cast<uint16_t*>(out), lse, H, nq, n, ncols, rs, hs);
+                           static_cast<uint16_t*>(out), lse, H, nq, n, ncols, rs, hs, dn);
     else
         hipLaunchKernelGGL((merge_kernel<32>), grid, dim3(256), 0, stream, part_o, part_ml,
-                           static_cast<uint16_t*>(out), lse, H, nq, n, ncols, rs, hs);
+                           static_cast<uint16_t*>(out), lse, H, nq, n, ncols, rs, hs, dn);
     return hipGetLastError();
 }
 

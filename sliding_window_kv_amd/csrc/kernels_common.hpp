@@ -71,6 +71,21 @@ struct SegList {
     int total_tiles;
 };
 
+// Ring plan of one streaming step in device memory.  The kernels of a
+// captured step read their destination rows, metadata entries and key
+// segments from here, so that one captured graph serves every frame.
+struct StepPlan {
+    int32_t row0;            // append: first destination row (slot * P)
+    int32_t append_meta;     // append: int32 index into the layer's metadata receiving the frame id
+    int32_t frame;           // frame id of the appended frame
+    int32_t retain;          // 1: copy the displaced frame's special rows before the append
+    int32_t retain_src;      // first special row of the displaced frame
+    int32_t retain_dst;      // first row of its entry in the special ring
+    int32_t retain_meta;     // int32 index into the metadata receiving the displaced frame id
+    int32_t victim_frame;
+    SegList seg;             // visible key segments after the append (and eviction)
+};
+
 struct AttnParams {
     const void* q;           // [nq_total, H, D] NHD
     const void* kreg;        // [H][rows][D]
@@ -94,6 +109,7 @@ struct AttnParams {
     int S;
     int fP;                  // key rows per frame in the region
     SegList seg;             // streaming only
+    const SegList* dseg;     // streaming: the segments in device memory instead of seg (captured steps)
 };
 
 }  // namespace swa

@@ -115,8 +115,14 @@ __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, co
                                                      T* __restrict__ kreg, T* __restrict__ vreg,
                                                      T* __restrict__ q, const int32_t* __restrict__ pos,
                                                      RopeArgs rope, NormArgs norm, int H, int n_tok, int row0,
-                                                     int rows, int32_t* meta_slot, int32_t frame_id) {
+                                                     int rows, int32_t* meta_slot, int32_t frame_id,
+                                                     const StepPlan* __restrict__ plan) {
     constexpr int E = Elt<T>::kPer16B;
+    if (plan != nullptr) {                   // captured step: destination and frame id from the device plan
+        row0 = plan->row0;
+        meta_slot += plan->append_meta;
+        frame_id = plan->frame;
+    }
     constexpr int CPR = D / E;               // 16-byte chunks per row
     constexpr int LD = D + 2;                // padded LDS row
     __shared__ T vt[kTileRows * LD];
@@ -216,7 +222,14 @@ __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, co
 template <typename T, int D>
 __global__ __launch_bounds__(256) void retain_kernel(T* __restrict__ kreg, T* __restrict__ vreg, int rows,
                                                      int src_row, int dst_row, int ns, int32_t* meta_slot,
-                                                     int32_t frame_id) {
+                                                     int32_t frame_id, const StepPlan* __restrict__ plan) {
+    if (plan != nullptr) {                   // captured step: the copy, if any, from the device plan
+        if (plan->retain == 0) return;
+        src_row = plan->retain_src;
+        dst_row = plan->retain_dst;
+        meta_slot += plan->retain_meta;
+        frame_id = plan->victim_frame;
+    }
     const int h = blockIdx.x;
     if (meta_slot != nullptr && h == 0 && threadIdx.x == 0) *meta_slot = frame_id;
     T* kh = kreg + static_cast<size_t>(h) * rows * D;
@@ -360,9 +373,12 @@ __global__ __launch_bounds__(256) void mask_kernel(int F, int P, int W, int S, i
 template <typename T, int D>
 hipError_t append_dispatch(int H, int n_tok, int row0, int rows, const void* k, const void* v,
                            void* kreg, void* vreg, void* q, const int32_t* pos, const RopeArgs* rope,
-                           const NormArgs* norm, int32_t* meta_slot, int32_t frame_id, hipStream_t stream) {
+                           const NormArgs* norm, int32_t* meta_slot, int32_t frame_id, const StepPlan* plan,
+                           hipStream_t stream) {
     const int first = row0 & ~15;
-    const int tiles = (row0 + n_tok - first + kTileRows - 1) / kTileRows;
+    // with a device plan the first row is not known here: enough tiles for any 16-row offset
+    const int tiles = plan != nullptr ? (15 + n_tok + kTileRows - 1) / kTileRows
+                                      : (row0 + n_tok - first + kTileRows - 1) / kTileRows;
     dim3 grid(tiles, H);
     RopeArgs r{};
     if (rope != nullptr) r = *rope;
@@ -371,7 +387,7 @@ hipError_t append_dispatch(int H, int n_tok, int row0, int rows, const void* k, 
 #define SWA_APPEND(RO, NO)                                                                                  \
     hipLaunchKernelGGL((append_kernel<T, D, RO, NO>), grid, dim3(256), 0, stream, static_cast<const T*>(k),  \
                        static_cast<const T*>(v), static_cast<T*>(kreg), static_cast<T*>(vreg), static_cast<T*>(q), \
-                       pos, r, nm, H, n_tok, row0, rows, meta_slot, frame_id)
+                       pos, r, nm, H, n_tok, row0, rows, meta_slot, frame_id, plan)
     if (rope != nullptr && norm != nullptr)
         SWA_APPEND(true, true);
     else if (rope != nullptr)
@@ -389,19 +405,37 @@ hipError_t append_dispatch(int H, int n_tok, int row0, int rows, const void* k, 
 hipError_t launch_append(int dtype, int H, int D, int n_tok, int row0, int rows, const void* k,
                          const void* v, void* kreg, void* vreg, void* q, const int32_t* pos,
                          const RopeArgs* rope, const NormArgs* norm, int32_t* meta_slot, int32_t frame_id,
-                         hipStream_t stream) {
+                         const StepPlan* plan, hipStream_t stream) {
     if (dtype == 0) {
         if (D == 64)
             return append_dispatch<uint16_t, 64>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm,
-                                                 meta_slot, frame_id, stream);
+                                                 meta_slot, frame_id, plan, stream);
         return append_dispatch<uint16_t, 32>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm,
-                                             meta_slot, frame_id, stream);
+                                             meta_slot, frame_id, plan, stream);
     }
     if (D == 64)
         return append_dispatch<float, 64>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm, meta_slot,
-                                          frame_id, stream);
+                                          frame_id, plan, stream);
     return append_dispatch<float, 32>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm, meta_slot,
-                                      frame_id, stream);
+                                      frame_id, plan, stream);
+}
+
+namespace {
+
+// One streaming step's ring plan into device memory (arguments by value, so
+// a later step's plan cannot overwrite this one before the launch).
+__global__ __launch_bounds__(64) void plan_store_kernel(StepPlan plan, StepPlan* __restrict__ dst) {
+    constexpr int N = static_cast<int>(sizeof(StepPlan) / 4);
+    static_assert(N <= 64, "one wave stores the plan");
+    const int i = threadIdx.x;
+    if (i < N) reinterpret_cast<int32_t*>(dst)[i] = reinterpret_cast<const int32_t*>(&plan)[i];
+}
+
+}  // namespace
+
+hipError_t launch_plan_store(const StepPlan& plan, StepPlan* dst, hipStream_t stream) {
+    hipLaunchKernelGGL(plan_store_kernel, dim3(1), dim3(64), 0, stream, plan, dst);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_append(int D, int nh, int rows, int slot, const void* k, const void* v, void* kreg,
@@ -441,26 +475,26 @@ hipError_t launch_qknorm(int dtype, int n_tok, int H, int D, void* q, void* k, c
 }
 
 hipError_t launch_retain(int dtype, int H, int D, int rows, int src_row, int dst_row, int ns,
-                         void* kreg, void* vreg, int32_t* meta_slot, int32_t frame_id,
+                         void* kreg, void* vreg, int32_t* meta_slot, int32_t frame_id, const StepPlan* plan,
                          hipStream_t stream) {
     if (dtype == 0) {
         if (D == 64)
             hipLaunchKernelGGL((retain_kernel<uint16_t, 64>), dim3(H), dim3(256), 0, stream,
                                static_cast<uint16_t*>(kreg), static_cast<uint16_t*>(vreg), rows, src_row,
-                               dst_row, ns, meta_slot, frame_id);
+                               dst_row, ns, meta_slot, frame_id, plan);
         else
             hipLaunchKernelGGL((retain_kernel<uint16_t, 32>), dim3(H), dim3(256), 0, stream,
                                static_cast<uint16_t*>(kreg), static_cast<uint16_t*>(vreg), rows, src_row,
-                               dst_row, ns, meta_slot, frame_id);
+                               dst_row, ns, meta_slot, frame_id, plan);
     } else {
         if (D == 64)
             hipLaunchKernelGGL((retain_kernel<float, 64>), dim3(H), dim3(256), 0, stream,
                                static_cast<float*>(kreg), static_cast<float*>(vreg), rows, src_row, dst_row,
-                               ns, meta_slot, frame_id);
+                               ns, meta_slot, frame_id, plan);
         else
             hipLaunchKernelGGL((retain_kernel<float, 32>), dim3(H), dim3(256), 0, stream,
                                static_cast<float*>(kreg), static_cast<float*>(vreg), rows, src_row, dst_row,
-                               ns, meta_slot, frame_id);
+                               ns, meta_slot, frame_id, plan);
     }
     return hipGetLastError();
 }

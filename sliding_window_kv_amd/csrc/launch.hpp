@@ -26,19 +26,27 @@ struct NormArgs {
 // With norm != null, k is layer-normed per head on the way and q
 // ([n_tok, H, D]) in place; with rope != null, k is rotated on the way and q
 // in place (after the norm).  meta_slot, if not null, receives frame_id.
+// With plan != null (captured steps) row0, frame_id and the metadata entry
+// (meta_slot + plan->append_meta) are read from the device plan instead.
 hipError_t launch_append(int dtype, int H, int D, int n_tok, int row0, int rows, const void* k,
                          const void* v, void* kreg, void* vreg, void* q, const int32_t* pos,
                          const RopeArgs* rope, const NormArgs* norm, int32_t* meta_slot, int32_t frame_id,
-                         hipStream_t stream);
+                         const StepPlan* plan, hipStream_t stream);
+
+// Store one step's ring plan into device memory (read by the kernels of a
+// captured step).
+hipError_t launch_plan_store(const StepPlan& plan, StepPlan* dst, hipStream_t stream);
 
 // Per-head layer norm of q and/or k ([n_tok, H, D]) in place.
 hipError_t launch_qknorm(int dtype, int n_tok, int H, int D, void* q, void* k, const NormArgs& norm,
                          hipStream_t stream);
 
 // Copy `ns` rows starting at src_row of every head (K and V^T) to dst_row;
-// meta_slot, if not null, receives frame_id.
+// meta_slot, if not null, receives frame_id.  With plan != null the copy
+// happens only if plan->retain, with rows, id and metadata entry
+// (meta_slot + plan->retain_meta) from the device plan.
 hipError_t launch_retain(int dtype, int H, int D, int rows, int src_row, int dst_row, int ns,
-                         void* kreg, void* vreg, int32_t* meta_slot, int32_t frame_id,
+                         void* kreg, void* vreg, int32_t* meta_slot, int32_t frame_id, const StepPlan* plan,
                          hipStream_t stream);
 
 hipError_t launch_rope(int dtype, int n_tok, int H, int D, void* q, void* k, const int32_t* pos,
@@ -61,7 +69,9 @@ hipError_t launch_mask(int F, int P, int W, int S, int token_level, uint8_t* out
 
 // Attention: bf16 on MFMA or fp32 on the vector ALUs.  Streaming bf16 runs
 // p.ncols columns of p.qtiles work-groups (grid = ncols * qtiles); heads
-// split across columns leave partials for launch_merge.
+// split across columns leave partials for launch_merge.  Streaming bf16
+// with p.dseg != null reads the segments from device memory and uses the
+// first min(p.ncols, H * tiles) columns.
 hipError_t launch_attention(int dtype, int D, bool prefill, const AttnParams& p, int grid,
                             hipStream_t stream);
 int attention_q_tile(int dtype);
@@ -70,8 +80,10 @@ int attention_blocks_per_cu(int dtype, int D);
 
 // Combine the streaming partials of heads split across columns (n = key
 // tiles per head) into out [nq, H, D] bf16 and lse [H, nq] (may be null).
+// dn != null: n is read from device memory and the columns clamped to H * n,
+// as the attention kernel does with device segments.
 hipError_t launch_merge(int D, int H, int nq, int n, int ncols, const float* part_o, const float* part_ml, void* out,
-                        float* lse, int64_t rs, int64_t hs, hipStream_t stream);
+                        float* lse, int64_t rs, int64_t hs, const int* dn, hipStream_t stream);
 
 // Token decode over rolling buffers ([H = sequences x kv heads][rows][D] and
 // V^T): the streaming attention kernel with one wave per work-group, whose

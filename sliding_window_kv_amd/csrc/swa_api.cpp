@@ -36,6 +36,7 @@ struct Layout {
     int max_records;
     int64_t k_bytes, v_bytes, meta_bytes, layer_bytes, work_offset, work_bytes;
     int64_t meta_pending, meta_special, meta_records;   // int32 offsets inside meta
+    int64_t plan_offset;                                 // device step plan (captured steps), in the work area
     int64_t total_bytes;
     int64_t part_o_floats;                               // floats of the O partials
 };
@@ -102,9 +103,12 @@ Layout make_layout(const swa_config* c) {
         const int64_t pieces = 2 * int64_t(swa::kMaxCols);   // two partial slots per column
         L.part_o_floats = pieces * L.P * L.D;
         L.work_bytes = align_up(L.part_o_floats * 4, 256) + align_up(pieces * L.P * 2 * 4, 256);
+        L.plan_offset = L.work_offset + L.work_bytes;
+        L.work_bytes += align_up(sizeof(swa::StepPlan), 256);
     } else {
         L.part_o_floats = 0;
         L.work_bytes = 0;
+        L.plan_offset = -1;
     }
     L.total_bytes = L.work_offset + L.work_bytes;
     return L;
@@ -159,6 +163,18 @@ struct swa_cache {
     float* part_ml() const {
         return reinterpret_cast<float*>(pool + L.work_offset + align_up(L.part_o_floats * 4, 256));
     }
+    swa::StepPlan* step_plan() const { return reinterpret_cast<swa::StepPlan*>(pool + L.plan_offset); }
+};
+
+// A captured streaming step of every layer (swa_graph_create).
+struct swa_graph {
+    swa_cache* c = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    ~swa_graph() {
+        if (exec != nullptr) (void)hipGraphExecDestroy(exec);
+        if (graph != nullptr) (void)hipGraphDestroy(graph);
+    }
 };
 
 namespace {
@@ -197,23 +213,45 @@ int enqueue_append(swa_cache* c, int layer, const swa::AppendPlan& plan, int64_t
         const int dst = L.special_row_base + plan.special_slot * L.ns;
         hipError_t e = swa::launch_retain(dt, L.H, L.D, L.rows, src, dst, L.ns, c->kreg(layer), c->vreg(layer),
                                           c->meta(layer) + L.meta_special + plan.special_id_index,
-                                          static_cast<int32_t>(plan.victim_frame), stream);
+                                          static_cast<int32_t>(plan.victim_frame), nullptr, stream);
         if (e != hipSuccess) return hip_fail(e, "retain kernel launch");
     }
     int32_t* slot_meta = plan.keyframe ? c->meta(layer) + plan.ord_index : c->meta(layer) + L.meta_pending;
     hipError_t e = swa::launch_append(dt, L.H, L.D, L.P, plan.slot * L.P, L.rows, k, v, c->kreg(layer),
                                       c->vreg(layer), q, pos, pos != nullptr ? &c->rope : nullptr, norm, slot_meta,
-                                      static_cast<int32_t>(t), stream);
+                                      static_cast<int32_t>(t), nullptr, stream);
     if (e != hipSuccess) return hip_fail(e, "append kernel launch");
     return SWA_OK;
 }
 
-// Attention of q over the layer's visible rows (split-KV + combine for bf16).
-int enqueue_attention(swa_cache* c, int layer, const void* q, void* out, float* lse, hipStream_t stream) {
-    const swa::Ring& ring = c->rings[layer];
-    const Layout& L = c->L;
+// The ring's visible rows as the kernels' segment list (tiles numbered
+// across segments in key order).
+int fill_segs(const swa::Ring& ring, swa::SegList* out) {
     std::vector<swa::RowSeg> segs;
     ring.segments(&segs);
+    if (segs.size() > static_cast<size_t>(swa::kMaxSegs)) return fail(SWA_E_STATE, "internal: bad segment list");
+    if (segs.empty()) return fail(SWA_E_STATE, "no cached frame to attend to");
+    out->n = static_cast<int>(segs.size());
+    int tiles = 0;
+    for (int i = 0; i < swa::kMaxSegs; ++i) {
+        if (i < out->n) {
+            out->lo[i] = segs[i].lo;
+            out->hi[i] = segs[i].hi;
+            out->tile0[i] = tiles;
+            tiles += tiles_of(segs[i].lo, segs[i].hi);
+        } else {
+            out->lo[i] = out->hi[i] = 0;
+            out->tile0[i] = 1 << 30;
+        }
+    }
+    out->total_tiles = tiles;
+    return SWA_OK;
+}
+
+// Attention parameters of one layer's frame query (everything but the
+// segments and the column count).
+swa::AttnParams frame_attn_params(const swa_cache* c, int layer, const void* q, void* out, float* lse) {
+    const Layout& L = c->L;
     swa::AttnParams p{};
     p.q = q;
     p.kreg = c->kreg(layer);
@@ -227,32 +265,64 @@ int enqueue_attention(swa_cache* c, int layer, const void* q, void* out, float* 
     p.rows = L.rows;
     p.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(L.D)));
     p.F = 1;
-    p.seg.n = static_cast<int>(segs.size());
-    int tiles = 0;
-    for (int i = 0; i < swa::kMaxSegs; ++i) {
-        if (i < p.seg.n) {
-            p.seg.lo[i] = segs[i].lo;
-            p.seg.hi[i] = segs[i].hi;
-            p.seg.tile0[i] = tiles;
-            tiles += tiles_of(segs[i].lo, segs[i].hi);
-        } else {
-            p.seg.lo[i] = p.seg.hi[i] = 0;
-            p.seg.tile0[i] = 1 << 30;
-        }
-    }
-    p.seg.total_tiles = tiles;
-    if (p.seg.n > swa::kMaxSegs) return fail(SWA_E_STATE, "internal: bad segment list");
-    if (p.seg.n == 0) return fail(SWA_E_STATE, "no cached frame to attend to");
     const int qrows = swa::attention_q_tile(c->cfg.dtype);
     p.qtiles = (L.P + qrows - 1) / qrows;
+    if (c->cfg.dtype == SWA_BF16) {
+        p.part_o = c->part_o();
+        p.part_ml = c->part_ml();
+    }
+    return p;
+}
+
+// Attention of q over the layer's visible rows (split-KV + combine for bf16).
+int enqueue_attention(swa_cache* c, int layer, const void* q, void* out, float* lse, hipStream_t stream) {
+    const Layout& L = c->L;
+    swa::AttnParams p = frame_attn_params(c, layer, q, out, lse);
+    const int rc = fill_segs(c->rings[layer], &p.seg);
+    if (rc != SWA_OK) return rc;
+    const int tiles = p.seg.total_tiles;
     p.ncols = c->cfg.dtype == SWA_BF16 ? pick_columns(c, p.qtiles, tiles) : 1;
-    p.part_o = c->part_o();
-    p.part_ml = c->part_ml();
     hipError_t e = swa::launch_attention(c->cfg.dtype, L.D, false, p, p.ncols * p.qtiles, stream);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
     // every head inside one column (ncols divides H): no partials to merge
     if (c->cfg.dtype == SWA_BF16 && !(p.ncols <= L.H && L.H % p.ncols == 0)) {
-        e = swa::launch_merge(L.D, L.H, L.P, tiles, p.ncols, p.part_o, p.part_ml, out, lse, p.rs, p.hs, stream);
+        e = swa::launch_merge(L.D, L.H, L.P, tiles, p.ncols, p.part_o, p.part_ml, out, lse, p.rs, p.hs, nullptr,
+                              stream);
+        if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    }
+    return SWA_OK;
+}
+
+// One layer's step with every ring-dependent value read from the device
+// step plan, for capture: retain (a no-op unless the plan asks), append
+// (+ norm, + RoPE), attention over the plan's segments on a fixed number of
+// columns, merge.
+int enqueue_planned_layer(swa_cache* c, int layer, void* q, const void* k, const void* v, const int32_t* pos,
+                          const swa::NormArgs* norm, void* out, float* lse, hipStream_t stream) {
+    const Layout& L = c->L;
+    const int dt = c->cfg.dtype;
+    const swa::StepPlan* plan = c->step_plan();
+    hipError_t e;
+    if (c->cfg.cross_frame_special) {
+        e = swa::launch_retain(dt, L.H, L.D, L.rows, 0, 0, L.ns, c->kreg(layer), c->vreg(layer), c->meta(layer), 0,
+                               plan, stream);
+        if (e != hipSuccess) return hip_fail(e, "retain kernel launch");
+    }
+    e = swa::launch_append(dt, L.H, L.D, L.P, 0, L.rows, k, v, c->kreg(layer), c->vreg(layer), q, pos,
+                           pos != nullptr ? &c->rope : nullptr, norm, c->meta(layer), 0, plan, stream);
+    if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+    swa::AttnParams p = frame_attn_params(c, layer, q, out, lse);
+    p.dseg = &plan->seg;
+    // the automatic (or fixed-split) column count before the clamp to the
+    // tile space, which the kernels apply on the device
+    p.ncols = static_cast<int>(std::min<int64_t>(
+        c->splits > 0 ? int64_t(L.H) * c->splits : std::max(1, c->num_cus * c->blocks_per_cu / std::max(1, p.qtiles)),
+        swa::kMaxCols));
+    e = swa::launch_attention(dt, L.D, false, p, p.ncols * p.qtiles, stream);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    if (!(p.ncols <= L.H && L.H % p.ncols == 0)) {
+        e = swa::launch_merge(L.D, L.H, L.P, 1, p.ncols, p.part_o, p.part_ml, out, lse, p.rs, p.hs,
+                              &plan->seg.total_tiles, stream);
         if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     }
     return SWA_OK;
@@ -635,7 +705,7 @@ int swa_decode_step(void* cache, size_t cache_bytes, int B, int Hq, int Hkv, int
     e = swa::launch_attention_decode(D, p, p.ncols, stream);
     if (e != hipSuccess) return hip_fail(e, "decode attention kernel launch");
     if (!(p.ncols <= nh && nh % p.ncols == 0)) {
-        e = swa::launch_merge(D, nh, G, tiles, p.ncols, p.part_o, p.part_ml, out, lse, p.rs, p.hs, stream);
+        e = swa::launch_merge(D, nh, G, tiles, p.ncols, p.part_o, p.part_ml, out, lse, p.rs, p.hs, nullptr, stream);
         if (e != hipSuccess) return hip_fail(e, "decode merge kernel launch");
     }
     return SWA_OK;
@@ -666,7 +736,7 @@ int swa_prefill_masked(const void* q, const void* k, const void* v, int F, int P
     void* vreg = static_cast<char*>(ws) + need / 2;
     // the F frames laid out as consecutive pages (frame f in rows [f*P, (f+1)*P))
     hipError_t e = swa::launch_append(dtype, H, D, F * P, 0, rows, k, v, kreg, vreg, nullptr, nullptr, nullptr, nullptr,
-                                      nullptr, 0, stream);
+                                      nullptr, 0, nullptr, stream);
     if (e != hipSuccess) return hip_fail(e, "chunk layout kernel launch");
     swa::AttnParams p{};
     p.q = q;
@@ -699,6 +769,127 @@ int swa_prefill_mask(int F, int P, int sws, int nfpb, int S, int token_level, ui
     const int W = sws == -1 ? -1 : sws * nfpb;
     hipError_t e = swa::launch_mask(F, P, W, S, token_level ? 1 : 0, dev_out, stream);
     if (e != hipSuccess) return hip_fail(e, "mask kernel launch");
+    return SWA_OK;
+}
+
+int swa_graph_create(swa_cache* c, void* const* q, const void* const* k, const void* const* v, void* const* out,
+                     float* const* lse, const int32_t* pos, const float* const* qk_norm_weights, float eps,
+                     swa_graph** g) {
+    if (g == nullptr) return fail(SWA_E_INVAL, "null output handle");
+    *g = nullptr;
+    if (c == nullptr) return fail(SWA_E_INVAL, "null cache");
+    if (c->dry) return fail(SWA_E_STATE, "bookkeeping-only cache cannot capture a step");
+    if (c->cfg.dtype != SWA_BF16) return fail(SWA_E_UNSUPPORTED, "captured steps need a bf16 cache");
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return fail(SWA_E_INVAL, "null tensor array");
+    const int nl = c->cfg.num_layers;
+    for (int l = 0; l < nl; ++l) {
+        if (q[l] == nullptr || k[l] == nullptr || v[l] == nullptr || out[l] == nullptr)
+            return fail(SWA_E_INVAL, "null tensor");
+        if (qk_norm_weights != nullptr && qk_norm_weights[l] == nullptr) return fail(SWA_E_INVAL, "null norm weights");
+    }
+    if (qk_norm_weights != nullptr && !(eps >= 0.f)) return fail(SWA_E_INVAL, "norm epsilon must be >= 0");
+    if (pos != nullptr && c->cfg.rope_pairs_t + c->cfg.rope_pairs_h + c->cfg.rope_pairs_w == 0)
+        return fail(SWA_E_INVAL, "positions given but the config has no rope bands");
+    // one plan serves every layer: their rings must be in the same state
+    const swa::RingCounters c0 = c->rings[0].counters();
+    if (c0.pending) return fail(SWA_E_STATE, "a non-keyframe is pending");
+    std::vector<swa::PageRec> p0, pl;
+    c->rings[0].pages(&p0);
+    for (int l = 1; l < nl; ++l) {
+        c->rings[l].pages(&pl);
+        const swa::RingCounters cl = c->rings[l].counters();
+        bool same = cl.n_key == c0.n_key && cl.n_win == c0.n_win && cl.n_special == c0.n_special &&
+                    pl.size() == p0.size();
+        for (size_t i = 0; same && i < pl.size(); ++i)
+            same = pl[i].frame == p0[i].frame && pl[i].slot == p0[i].slot && pl[i].row0 == p0[i].row0 &&
+                   pl[i].nrows == p0[i].nrows && pl[i].region == p0[i].region;
+        if (!same) return fail(SWA_E_STATE, "layers are in different ring states");
+    }
+
+    swa_graph* gr = new (std::nothrow) swa_graph();
+    if (gr == nullptr) return fail(SWA_E_INVAL, "out of host memory");
+    gr->c = c;
+    hipStream_t s = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    if (e != hipSuccess) {
+        delete gr;
+        return hip_fail(e, "capture stream");
+    }
+    e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+    int rc = e == hipSuccess ? SWA_OK : hip_fail(e, "begin capture");
+    for (int l = 0; rc == SWA_OK && l < nl; ++l) {
+        swa::NormArgs norm{qk_norm_weights != nullptr ? qk_norm_weights[l] : nullptr, eps};
+        rc = enqueue_planned_layer(c, l, q[l], k[l], v[l], pos, qk_norm_weights != nullptr ? &norm : nullptr,
+                                   out[l], lse != nullptr ? lse[l] : nullptr, s);
+    }
+    if (e == hipSuccess) {
+        const hipError_t e2 = hipStreamEndCapture(s, &gr->graph);
+        if (rc == SWA_OK && e2 != hipSuccess) rc = hip_fail(e2, "end capture");
+    }
+    if (rc == SWA_OK) {
+        e = hipGraphInstantiate(&gr->exec, gr->graph, nullptr, nullptr, 0);
+        if (e != hipSuccess) rc = hip_fail(e, "graph instantiate");
+    }
+    (void)hipStreamDestroy(s);
+    if (rc != SWA_OK) {
+        delete gr;
+        return rc;
+    }
+    *g = gr;
+    return SWA_OK;
+}
+
+int swa_graph_step(swa_graph* g, int64_t t, int keyframe, swa_stream_t stream) {
+    if (g == nullptr) return fail(SWA_E_INVAL, "null graph");
+    swa_cache* c = g->c;
+    const Layout& L = c->L;
+    const int nl = c->cfg.num_layers;
+    const swa::RingCounters c0 = c->rings[0].counters();
+    for (int l = 1; l < nl; ++l) {
+        const swa::RingCounters cl = c->rings[l].counters();
+        if (cl.n_key != c0.n_key || cl.n_win != c0.n_win || cl.n_special != c0.n_special || cl.pending != c0.pending)
+            return fail(SWA_E_STATE, "layers are in different ring states");
+    }
+    swa::AppendPlan plan;
+    std::string err;
+    int rc = c->rings[0].plan_append(t, keyframe != 0, &plan, &err);
+    if (rc != SWA_OK) return fail(rc, err);
+    // the ring as the attention sees it: after the append and, for a
+    // keyframe, the eviction
+    swa::Ring seen = c->rings[0];
+    seen.commit_append(plan, t);
+    if (keyframe) seen.evict();
+    swa::StepPlan sp{};
+    rc = fill_segs(seen, &sp.seg);
+    if (rc != SWA_OK) return rc;
+    sp.row0 = plan.slot * L.P;
+    sp.append_meta = plan.keyframe ? plan.ord_index : static_cast<int32_t>(L.meta_pending);
+    sp.frame = static_cast<int32_t>(t);
+    sp.retain = plan.retain ? 1 : 0;
+    if (plan.retain) {
+        sp.retain_src = plan.victim_slot * L.P + c->cfg.special_row0;
+        sp.retain_dst = L.special_row_base + plan.special_slot * L.ns;
+        sp.retain_meta = static_cast<int32_t>(L.meta_special + plan.special_id_index);
+        sp.victim_frame = static_cast<int32_t>(plan.victim_frame);
+    }
+    hipError_t e = swa::launch_plan_store(sp, c->step_plan(), stream);
+    if (e != hipSuccess) return hip_fail(e, "step plan store");
+    e = hipGraphLaunch(g->exec, stream);
+    if (e != hipSuccess) return hip_fail(e, "graph launch");
+    for (int l = 0; l < nl; ++l) {
+        c->rings[l].commit_append(plan, t);
+        if (keyframe) {
+            c->rings[l].evict();
+        } else {
+            rc = c->rings[l].rollback(&err);
+            if (rc != SWA_OK) return fail(rc, err);
+        }
+    }
+    return SWA_OK;
+}
+
+int swa_graph_destroy(swa_graph* g) {
+    delete g;
     return SWA_OK;
 }
 

@@ -1,6 +1,7 @@
 """C-ABI checks that need no GPU: exported symbols, argument validation and
 the host ring bookkeeping (page lists bit-exact against the oracle's naive
-ring cache).  Only bookkeeping-only caches are used here; no kernel runs."""
+ring cache).  Caches are bookkeeping-only, or placed at a fake pool address
+for argument checks that fail before anything is enqueued; no kernel runs."""
 import ctypes
 
 import numpy as np
@@ -238,3 +239,34 @@ def test_capacity_error_with_window_off():
     swa.kvcache_append(h, 0, 4, None, None, False)
     assert swa.kvcache_visible_pages(h, 0)[-1] == (4, 0, 3, 0, 5)
     swa.swa_cache_destroy(h)
+
+
+def test_graph_argument_checks():
+    # a cache over a fake (never dereferenced) pool address: every call below
+    # fails its argument or state check before anything is enqueued
+    fake = ctypes.c_void_p(1 << 20)
+    a4 = [256, 256]
+    c = swa.make_config(21, 2, 32, num_layers=2, sliding_window_size=2, scale_frames=1, dtype=swa.SWA_F32)
+    h = swa.swa_cache_create(c, fake, swa.swa_cache_pool_bytes(c))
+    with pytest.raises(swa.SwaError) as e:
+        swa.swa_graph_create(h, a4, a4, a4, a4, None, None, None, 1e-5)
+    assert e.value.code == swa.SWA_E_UNSUPPORTED
+    swa.swa_cache_destroy(h)
+    c = swa.make_config(21, 2, 32, num_layers=2, sliding_window_size=2, scale_frames=1)
+    h = swa.swa_cache_create(c, fake, swa.swa_cache_pool_bytes(c))
+    for args in [([256, None], a4, a4, a4, None, None, None, 1e-5),          # null tensor
+                 (a4, a4, a4, a4, None, ctypes.c_void_p(256), None, 1e-5),  # positions without rope bands
+                 (a4, a4, a4, a4, None, None, a4, -1.0),                    # negative epsilon
+                 (a4, a4, a4, a4, None, None, [256, None], 1e-5)]:          # null norm weights
+        with pytest.raises(swa.SwaError) as e:
+            swa.swa_graph_create(h, *args)
+        assert e.value.code == swa.SWA_E_INVAL
+    swa.swa_cache_destroy(h)
+    d = swa.swa_cache_create(c, None, 0)
+    with pytest.raises(swa.SwaError) as e:
+        swa.swa_graph_create(d, a4, a4, a4, a4, None, None, None, 1e-5)
+    assert e.value.code == swa.SWA_E_STATE
+    with pytest.raises(swa.SwaError) as e:
+        swa.swa_graph_step(None, 0, 1)
+    assert e.value.code == swa.SWA_E_INVAL
+    swa.swa_cache_destroy(d)
