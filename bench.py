@@ -27,6 +27,8 @@ frame's ring page) + evict + attention (splits merged in-kernel), through the C 
             run as a separate norm kernel followed by the RoPE + append
   decode    token decode, 32 query heads over 8 kv heads, a 4096-slot
             rolling buffer per sequence, batch 16 (and batch 1), buffer full
+  graph     the headline step for 12 layers as one captured graph replayed
+            per frame, against the same 12 layers stepped one call each
 """
 from __future__ import annotations
 
@@ -345,6 +347,70 @@ def bench_normed(args, torch, swa):
 
 
 # ---------------------------------------------------------------------------
+# captured multi-layer step
+# ---------------------------------------------------------------------------
+
+def bench_graph(args, torch, swa):
+    from swa_synth import frame_qkv
+    L, P, H, D, W, S = 12, 1374, 16, 64, 16, 8
+    cfg = swa.make_config(P, H, D, sliding_window_size=W, scale_frames=S, num_layers=L)
+    gcache, ecache = swa.SwaCache(cfg), swa.SwaCache(cfg)
+    if args.splits is not None:
+        gcache.set_splits(args.splits)
+        ecache.set_splits(args.splits)
+    qkv = [_dev(torch, frame_qkv(9, l, P, H, D)) for l in range(L)]   # one frame per layer, re-appended each step
+    outs = [torch.empty((P, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    graph = swa.SwaGraph(gcache, [x[0] for x in qkv], [x[1] for x in qkv], [x[2] for x in qkv], outs)
+    state = {"g": 0, "e": 0}
+
+    def step_graph(_):
+        graph.step(state["g"], True)
+        state["g"] += 1
+
+    def step_eager(_):
+        t = state["e"]
+        for l in range(L):
+            q, k, v = qkv[l]
+            ecache.step(l, t, q, k, v, True, outs[l], None)
+        state["e"] = t + 1
+
+    for _ in range(S + W + args.warmup):
+        step_graph(0)
+        step_eager(0)
+    keys = sum(p[4] for p in gcache.pages(0))
+    assert keys == (S + W) * P
+    flops = 4.0 * D * H * P * keys * L
+    ms = _timed(torch, step_graph, args.steps)
+    ms_eager = _timed(torch, step_eager, args.steps)
+
+    def host_ms(fn, reps=15, n=3):
+        """Host time to enqueue one step: median over bursts of n steps, each
+        started on an idle GPU (the queue never fills)."""
+        per = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(n):
+                fn(0)
+            per.append((time.perf_counter() - t0) / n * 1e3)
+        torch.cuda.synchronize()
+        return sorted(per)[len(per) // 2]
+
+    host_graph, host_eager = host_ms(step_graph), host_ms(step_eager)
+    graph.close()
+    res = _base(args, f"captured {L}-layer streaming step, TFLOP/s (1374 q x 32,976 keys per layer)",
+                flops / (ms * 1e-3) / 1e12, "TFLOP/s", ms,
+                {"workload": "graph_step", "layers": L, "tokens_per_frame": P, "heads": H, "head_dim": D,
+                 "scale_frames": S, "window_frames": W, "visible_keys": keys})
+    res["frames_per_s_per_layer"] = round(1000.0 * L / ms, 1)
+    res["eager_ms_per_step"] = round(ms_eager, 5)
+    res["eager_frames_per_s_per_layer"] = round(1000.0 * L / ms_eager, 1)
+    res["launches_per_step"] = {"captured": 2, "eager": 3 * L}
+    res["host_enqueue_ms_per_step"] = {"captured": round(host_graph, 4), "eager": round(host_eager, 4)}
+    return res
+
+
+# ---------------------------------------------------------------------------
 # token-level decode over rolling buffers (grouped-query heads)
 # ---------------------------------------------------------------------------
 
@@ -441,7 +507,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="stream", choices=["stream", "prefill", "rope", "specials", "normed", "decode", "all"])
+    ap.add_argument("--workload", default="stream",
+                    choices=["stream", "prefill", "rope", "specials", "normed", "decode", "graph", "all"])
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
@@ -453,9 +520,10 @@ def main():
     import sliding_window_kv_amd as swa
     swa.lib()
     torch.cuda.set_device(0)
-    order = ["stream", "prefill", "rope", "specials", "normed", "decode"] if args.workload == "all" else [args.workload]
+    order = (["stream", "prefill", "rope", "specials", "normed", "decode", "graph"] if args.workload == "all"
+             else [args.workload])
     fns = {"stream": bench_stream, "prefill": bench_prefill, "rope": bench_rope, "specials": bench_specials,
-           "normed": bench_normed, "decode": bench_decode}
+           "normed": bench_normed, "decode": bench_decode, "graph": bench_graph}
     for w in order:
         print(json.dumps(fns[w](args, torch, swa)), flush=True)
 
