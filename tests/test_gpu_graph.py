@@ -30,10 +30,13 @@ def _oracle_step(oc, t, q, k, v, keyframe, rows):
 
 
 def _run(P, H, D, W, S, L, T, keyframe_of=lambda t: True, cross=False, ns=5, R=1000, rope=(0, 0, 0),
-         grid=None, norm=False, rows=None, oracle_at=None):
+         grid=None, norm=False, rows=None, oracle_at=None, splits=None):
     cfg = swa.make_config(P, H, D, sliding_window_size=W, scale_frames=S, num_layers=L, cross_frame_special=cross,
                           special_rows=ns, max_special_frames=R, rope=rope)
     gcache, ecache = swa.SwaCache(cfg), swa.SwaCache(cfg)
+    if splits is not None:                   # before the capture: the column count is fixed in the graph
+        gcache.set_splits(splits)
+        ecache.set_splits(splits)
     qs = [torch.empty((P, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
     ks = [torch.empty_like(qs[0]) for _ in range(L)]
     vs = [torch.empty_like(qs[0]) for _ in range(L)]
@@ -103,6 +106,15 @@ def _run(P, H, D, W, S, L, T, keyframe_of=lambda t: True, cross=False, ns=5, R=1
 def test_graph_small_all_rows(D):
     case(f"graph step P=200 H=4 D={D} W=4 S=2, 3 layers, 12 frames")
     _run(200, 4, D, 4, 2, 3, 12)
+
+
+@pytest.mark.parametrize("splits", [1, 5])
+def test_graph_fixed_splits(splits):
+    # one piece per head (no merge launched), and five pieces per head: 20
+    # columns, more than the 16 (head, tile) units of the first frame, so the
+    # device clamps the column count as the per-layer path does on the host
+    case(f"graph step with {splits} pieces per head")
+    _run(200, 4, 64, 4, 2, 2, 9, splits=splits)
 
 
 def test_graph_specials_nonkeyframes_rope_norm():
