@@ -294,7 +294,8 @@ int swa_stream_step_normed(swa_cache* cache, int layer, int64_t frame_t, void* q
  *   buffer shared by the layers, rewritten by the caller per frame.
  *   qk_norm_weights: NULL (no norm) or a host array of num_layers device
  *   float [4][D] pointers; eps as in qk_norm_apply.  Every layer must be in
- *   the same ring state with no non-keyframe pending.  Capturing and
+ *   the same ring state with no non-keyframe pending.  The work split in
+ *   force (swa_cache_set_splits) is fixed into the graph.  Capturing and
  *   instantiating the graph lets the HIP runtime allocate its own
  *   resources; swa_graph_step allocates nothing.
  *   Errors: SWA_E_INVAL (null pointers, eps < 0, positions without rope

@@ -156,3 +156,36 @@ def test_graph_refuses_diverged_layers():
     torch.cuda.synchronize()
     assert c.pages(0) == c.pages(1) == [(3, swa.SWA_REGION_FRAME, 0, 0, P)]
     g.close()
+
+
+def test_graph_window_off_capacity():
+    # window off: every keyframe stays (slot = ordinal) up to max_frames,
+    # then the step is refused before anything is enqueued
+    P, H, D = 96, 2, 64
+    case("graph step, window off, capacity")
+    cfg = swa.make_config(P, H, D, sliding_window_size=-1, max_frames=3, num_layers=2)
+    gc, ec = swa.SwaCache(cfg), swa.SwaCache(cfg)
+    q = [torch.empty((P, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    k = [torch.empty_like(q[0]) for _ in range(2)]
+    v = [torch.empty_like(q[0]) for _ in range(2)]
+    o = [torch.empty_like(q[0]) for _ in range(2)]
+    g = swa.SwaGraph(gc, q, k, v, o)
+    for t in range(4):
+        kf = t != 1                              # frame 1 a non-keyframe: it is not kept
+        frames = [frame_qkv(300 + l, t, P, H, D) for l in range(2)]
+        for l, (a, b, c) in enumerate(frames):
+            q[l].copy_(dev(a))
+            k[l].copy_(dev(b))
+            v[l].copy_(dev(c))
+        g.step(t, kf)
+        for l, (a, b, c) in enumerate(frames):
+            oe = torch.empty_like(o[l])
+            ec.step(l, t, dev(a), dev(b), dev(c), kf, oe, None)
+            torch.cuda.synchronize()
+            assert torch.equal(o[l], oe), f"out layer {l} t={t}"
+    assert [p[0] for p in gc.pages(0)] == [0, 2, 3]
+    with pytest.raises(swa.SwaError) as e:
+        g.step(4, True)
+    assert e.value.code == swa.SWA_E_CAPACITY
+    assert gc.pages(1) == ec.pages(1)            # nothing advanced on the refused step
+    g.close()
