@@ -499,6 +499,32 @@ def bench_specials(args, torch, swa):
     res["keyframe_TFLOPs"] = round(fl_k / (ms_k * 1e-3) / 1e12, 2)
     res["nonkeyframe_TFLOPs"] = round(fl_n / (ms_n * 1e-3) / 1e12, 2)
     res["frames_per_s_per_layer"] = round(1000.0 / ms, 1)
+    # the visible-page list of the full ring (1,000 special entries) built on
+    # the device and read back (builder kernel + copy + synchronize), and the
+    # host ring bookkeeping of one keyframe step on a bookkeeping-only cache
+    # (append plan + evict, ctypes calls included)
+    lat = []
+    for _ in range(20):
+        t1 = time.perf_counter()
+        recs, n = cache.device_pages(0)
+        lat.append((time.perf_counter() - t1) * 1e3)
+    assert recs == cache.pages(0)
+    res["page_list_records"] = n
+    res["device_page_list_ms"] = round(sorted(lat)[len(lat) // 2], 4)
+    cfg = swa.make_config(P, H, D, sliding_window_size=W, scale_frames=S, cross_frame_special=True, special_row0=0,
+                          special_rows=ns, max_special_frames=R)
+    dry = swa.swa_cache_create(cfg, None, 0)
+    for t in range(t0):
+        swa.kvcache_append(dry, 0, t, None, None, True)
+        swa.kvcache_evict(dry, 0)
+    lat = []
+    for t in range(t0, t0 + 200):
+        t1 = time.perf_counter()
+        swa.kvcache_append(dry, 0, t, None, None, True)
+        swa.kvcache_evict(dry, 0)
+        lat.append((time.perf_counter() - t1) * 1e6)
+    swa.swa_cache_destroy(dry)
+    res["host_bookkeeping_us_per_keyframe"] = round(sorted(lat)[len(lat) // 2], 2)
     return res
 
 
