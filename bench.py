@@ -283,6 +283,13 @@ def bench_rope(args, torch, swa):
     res["p50_ms"] = round(_pct(times, 50), 5)
     res["p99_ms"] = round(_pct(times, 99), 5)
     res["fused_rope_append_bytes"] = 6 * P * H * D * 2
+    # the standalone 3-D RoPE pass (rope3d_apply on q and k in place) at the
+    # same shape: 4 x P x H x D x 2 B moved plus the positions
+    qr, kr = pool[0][0].clone(), pool[0][1].clone()
+    ms_rope = _timed(torch, lambda i: swa.rope3d_t(qr, kr, pos[i % T], (12, 10, 10)), max(args.steps, 1))
+    rope_bytes = 4 * P * H * D * 2 + 12 * P
+    res["rope_standalone_us"] = round(ms_rope * 1e3, 2)
+    res["rope_standalone_GBps"] = round(rope_bytes / (ms_rope * 1e-3) / 1e9, 1)
     return res
 
 
