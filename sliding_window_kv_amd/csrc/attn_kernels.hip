@@ -645,7 +645,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnParams p) {
 
 // Merge of the streaming partials: for head h the columns c_lo .. c_hi cover
 // its tiles, and column c holds its piece in slot 2c if head h is the first
-// head of the column, else in slot 2c + 1.
+// head of the column, else in slot 2c + 1.  Every column after c_lo starts
+// inside head h, so only c_lo can hold h's piece in its second slot: one
+// division per thread picks that slot (64-bit divisions are long
+// instruction sequences on the GPU).
 //   O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c,  M = max_c m_c.
 // Heads that lie inside one column were written by the attention kernel.
 __device__ __forceinline__ int column_of(int64_t x, int64_t hn, int ncols) {
@@ -672,20 +675,28 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     const int c_lo = column_of(a, hn, ncols);
     const int c_hi = column_of(a + n - 1, hn, ncols);
     if (c_lo == c_hi) return;
+    const int first = 2 * c_lo + (hn * c_lo / ncols >= a ? 0 : 1);
+    // one pass with a running max (unrolled so that several pieces' loads
+    // are in flight at once): M, Lsum and acc rescaled when M moves
     float M = -INFINITY;
-    for (int c = c_lo; c <= c_hi; ++c) {
-        const int piece = 2 * c + (hn * c / ncols >= a ? 0 : 1);
-        M = fmaxf(M, part_ml[(static_cast<size_t>(piece) * nq + r) * 2]);
-    }
     float Lsum = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
     for (int c = c_lo; c <= c_hi; ++c) {
-        const int piece = 2 * c + (hn * c / ncols >= a ? 0 : 1);
+        const int piece = c == c_lo ? first : 2 * c;
         const size_t row = static_cast<size_t>(piece) * nq + r;
         const float ms = part_ml[row * 2];
+        const float ls = part_ml[row * 2 + 1];
+        const f32x4 oc = *reinterpret_cast<const f32x4*>(part_o + row * D + chunk * 4);
+        if (ms > M) {
+            const float scale = __builtin_amdgcn_exp2f(M - ms);     // 0 while M = -inf
+            Lsum *= scale;
+            acc *= scale;
+            M = ms;
+        }
         const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-        Lsum += w * part_ml[row * 2 + 1];
-        acc += w * *reinterpret_cast<const f32x4*>(part_o + row * D + chunk * 4);
+        Lsum += w * ls;
+        acc += w * oc;
     }
     const float inv = 1.f / Lsum;
     const int64_t g = r * rs + h * hs + chunk * 4;
@@ -735,10 +746,8 @@ __global__ __launch_bounds__(256) void merge_wide_kernel(const float* __restrict
     const int c_hi = column_of(a + n - 1, hn, ncols);
     if (c_lo == c_hi) return;                       // whole head in one column: written by the attention kernel
     const int npc = c_hi - c_lo + 1;
-    auto piece_of = [&](int j) {
-        const int c = c_lo + j;
-        return 2 * c + (hn * c / ncols >= a ? 0 : 1);
-    };
+    const int first = 2 * c_lo + (hn * c_lo / ncols >= a ? 0 : 1);   // see merge_kernel
+    auto piece_of = [&](int j) { return j == 0 ? first : 2 * (c_lo + j); };
     for (int r = wave; r < nq; r += 4) {
         float M = -INFINITY;
         for (int j = lane; j < npc; j += 64)
@@ -770,6 +779,8 @@ __global__ __launch_bounds__(256) void merge_wide_kernel(const float* __restrict
         if (ok) {
             const int r = item / C;
             const int chunk = item % C;
+            // unrolled so that several pieces' loads are in flight at once
+#pragma unroll 4
             for (int j = pg; j < npc; j += PG) {
                 const size_t row = static_cast<size_t>(piece_of(j)) * nq + r;
                 acc += wts[r * npc + j] * *reinterpret_cast<const f32x4*>(part_o + row * D + chunk * 4);
