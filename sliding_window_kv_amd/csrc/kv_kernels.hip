@@ -133,60 +133,69 @@ __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, co
 
     if (meta_slot != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *meta_slot = frame_id;
 
-    for (int c = tid; c < kTileRows * CPR; c += 256) {
+    // Every thread's loads first, all in flight together; rows outside the
+    // frame read token 0 and store nothing (every lane also takes part in
+    // the norm's row reductions).
+    constexpr int NC = kTileRows * CPR / 256;
+    static_assert(NC * 256 == kTileRows * CPR, "whole 16-byte chunks per thread");
+    Chunk<T> kv[NC], vv[NC], qv[NC];
+#pragma unroll
+    for (int it = 0; it < NC; ++it) {
+        const int c = tid + it * 256;
+        const int tok = base + c / CPR - row0;
+        const int t = (tok >= 0 && tok < n_tok) ? tok : 0;
+        const size_t src = (static_cast<size_t>(t) * H + h) * D + (c % CPR) * E;
+        kv[it].u = *reinterpret_cast<const uint4*>(k + src);
+        vv[it].u = *reinterpret_cast<const uint4*>(v + src);
+        if constexpr (NORM || ROPE) qv[it].u = *reinterpret_cast<const uint4*>(q + src);
+    }
+    // consumed here, so that no load is sunk into the conditional stores below
+    // (it would then wait for the one before it)
+#pragma unroll
+    for (int it = 0; it < NC; ++it) {
+        asm volatile("" ::"v"(kv[it].u.x), "v"(kv[it].u.y), "v"(kv[it].u.z), "v"(kv[it].u.w));
+        asm volatile("" ::"v"(vv[it].u.x), "v"(vv[it].u.y), "v"(vv[it].u.z), "v"(vv[it].u.w));
+        if constexpr (NORM || ROPE)
+            asm volatile("" ::"v"(qv[it].u.x), "v"(qv[it].u.y), "v"(qv[it].u.z), "v"(qv[it].u.w));
+    }
+#pragma unroll
+    for (int it = 0; it < NC; ++it) {
+        const int c = tid + it * 256;
         const int rr = c / CPR;
         const int ch = c % CPR;
         const int r = base + rr;
         const int tok = r - row0;
-        Chunk<T> kv, vv;
+        const bool ok = tok >= 0 && tok < n_tok;
+        const int t = ok ? tok : 0;
+        const size_t src = (static_cast<size_t>(t) * H + h) * D + ch * E;
         if constexpr (NORM) {
-            // every lane takes part in the row reductions: rows outside the
-            // frame read token 0 and store nothing
-            const bool ok = tok >= 0 && tok < n_tok;
-            const int t = ok ? tok : 0;
-            const size_t src = (static_cast<size_t>(t) * H + h) * D + ch * E;
-            kv.u = *reinterpret_cast<const uint4*>(k + src);
-            vv.u = *reinterpret_cast<const uint4*>(v + src);
-            Chunk<T> qv;
-            qv.u = *reinterpret_cast<const uint4*>(q + src);
             float kf[E], qf[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                kf[e] = Elt<T>::ld(kv.e[e]);
-                qf[e] = Elt<T>::ld(qv.e[e]);
+                kf[e] = Elt<T>::ld(kv[it].e[e]);
+                qf[e] = Elt<T>::ld(qv[it].e[e]);
             }
             row_layer_norm<CPR, E>(qf, norm.w + ch * E, norm.w + D + ch * E, norm.eps);
             row_layer_norm<CPR, E>(kf, norm.w + 2 * D + ch * E, norm.w + 3 * D + ch * E, norm.eps);
             if constexpr (ROPE) rope_pairs2<E>(kf, qf, rope, pos + 3 * t, ch * E / 2);
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                kv.e[e] = Elt<T>::st(kf[e]);
-                qv.e[e] = Elt<T>::st(qf[e]);
+                kv[it].e[e] = Elt<T>::st(kf[e]);
+                qv[it].e[e] = Elt<T>::st(qf[e]);
             }
-            if (ok) {
-                *reinterpret_cast<uint4*>(q + src) = qv.u;
-                *reinterpret_cast<uint4*>(kreg + (static_cast<size_t>(h) * rows + r) * D + ch * E) = kv.u;
-            } else {
-                vv.u = make_uint4(0, 0, 0, 0);
-            }
-        } else if (tok >= 0 && tok < n_tok) {
-            const size_t src = (static_cast<size_t>(tok) * H + h) * D + ch * E;
-            kv.u = *reinterpret_cast<const uint4*>(k + src);
-            vv.u = *reinterpret_cast<const uint4*>(v + src);
-            if constexpr (ROPE) {
-                const int32_t* p3 = pos + 3 * tok;
-                rope_chunk<T>(kv.e, rope, p3, ch * E / 2);
-                Chunk<T> qv;
-                qv.u = *reinterpret_cast<const uint4*>(q + src);
-                rope_chunk<T>(qv.e, rope, p3, ch * E / 2);
-                *reinterpret_cast<uint4*>(q + src) = qv.u;
-            }
-            *reinterpret_cast<uint4*>(kreg + (static_cast<size_t>(h) * rows + r) * D + ch * E) = kv.u;
+        } else if constexpr (ROPE) {
+            const int32_t* p3 = pos + 3 * t;
+            rope_chunk<T>(kv[it].e, rope, p3, ch * E / 2);
+            rope_chunk<T>(qv[it].e, rope, p3, ch * E / 2);
+        }
+        if (ok) {
+            if constexpr (NORM || ROPE) *reinterpret_cast<uint4*>(q + src) = qv[it].u;
+            *reinterpret_cast<uint4*>(kreg + (static_cast<size_t>(h) * rows + r) * D + ch * E) = kv[it].u;
         } else {
-            vv.u = make_uint4(0, 0, 0, 0);
+            vv[it].u = make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
-        for (int e = 0; e < E; ++e) vt[rr * LD + ch * E + e] = vv.e[e];
+        for (int e = 0; e < E; ++e) vt[rr * LD + ch * E + e] = vv[it].e[e];
     }
     __syncthreads();
 
