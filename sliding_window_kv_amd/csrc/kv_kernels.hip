@@ -38,40 +38,60 @@ union Chunk {
     T e[Elt<T>::kPer16B];
 };
 
-// Angle of pair p for a token at position pos (band chosen by p), reduced to
-// [-pi, pi] in double before the single-precision sine and cosine.
-__device__ __forceinline__ void rope_cs(const RopeArgs& r, const int32_t* pos3, int p, float* c,
+// The token's three positions and the frequencies of pairs p0 .. p0+NP-1,
+// all loaded before any of them is used (the sine/cosine code between uses
+// would otherwise hold each next load back).
+template <int NP>
+struct RopeIn {
+    int pos[3];
+    double freq[NP];
+    RopeIn() = default;
+    __device__ RopeIn(const RopeArgs& r, const int32_t* pos3, int p0) {
+#pragma unroll
+        for (int b = 0; b < 3; ++b) pos[b] = pos3[b];
+#pragma unroll
+        for (int j = 0; j < NP; ++j) freq[j] = r.freq[p0 + j];
+    }
+};
+
+// Angle of pair p (band chosen by p) reduced to [-pi, pi] in double before
+// the single-precision sine and cosine.
+__device__ __forceinline__ void rope_cs(const RopeArgs& r, const int (&pos)[3], double freq, int p, float* c,
                                         float* s) {
     const int band = p < r.pairs_t ? 0 : (p < r.pairs_t + r.pairs_h ? 1 : 2);
-    const double a = static_cast<double>(pos3[band]) * r.freq[p];
+    const double a = static_cast<double>(band == 0 ? pos[0] : band == 1 ? pos[1] : pos[2]) * freq;
     const double twopi = 6.283185307179586476925286766559;
     const double red = a - twopi * rint(a * (1.0 / twopi));
     sincosf(static_cast<float>(red), s, c);
 }
 
-// Rotate the E elements (E/2 pairs) of one 16-byte chunk in place.
+// Rotate the E/2 pairs of one 16-byte chunk of k and one of q in place (the
+// angles of the token computed once for both).
 template <typename T>
-__device__ __forceinline__ void rope_chunk(T* x, const RopeArgs& r, const int32_t* pos3, int p0) {
+__device__ __forceinline__ void rope_chunk2(T* x, T* y, const RopeArgs& r, const RopeIn<Elt<T>::kPer16B / 2>& in,
+                                            int p0) {
     constexpr int E = Elt<T>::kPer16B;
 #pragma unroll
     for (int j = 0; j < E / 2; ++j) {
         float c, s;
-        rope_cs(r, pos3, p0 + j, &c, &s);
-        const float a = Elt<T>::ld(x[2 * j]);
-        const float b = Elt<T>::ld(x[2 * j + 1]);
+        rope_cs(r, in.pos, in.freq[j], p0 + j, &c, &s);
+        const float a = Elt<T>::ld(x[2 * j]), b = Elt<T>::ld(x[2 * j + 1]);
+        const float qa = Elt<T>::ld(y[2 * j]), qb = Elt<T>::ld(y[2 * j + 1]);
         x[2 * j] = Elt<T>::st(a * c - b * s);
         x[2 * j + 1] = Elt<T>::st(a * s + b * c);
+        y[2 * j] = Elt<T>::st(qa * c - qb * s);
+        y[2 * j + 1] = Elt<T>::st(qa * s + qb * c);
     }
 }
 
 // Rotate E/2 pairs of one chunk of k and one of q held as floats (the
 // angles of a token computed once for both).
 template <int E>
-__device__ __forceinline__ void rope_pairs2(float* x, float* y, const RopeArgs& r, const int32_t* pos3, int p0) {
+__device__ __forceinline__ void rope_pairs2(float* x, float* y, const RopeArgs& r, const RopeIn<E / 2>& in, int p0) {
 #pragma unroll
     for (int j = 0; j < E / 2; ++j) {
         float c, s;
-        rope_cs(r, pos3, p0 + j, &c, &s);
+        rope_cs(r, in.pos, in.freq[j], p0 + j, &c, &s);
         const float a = x[2 * j], b = x[2 * j + 1];
         x[2 * j] = a * c - b * s;
         x[2 * j + 1] = a * s + b * c;
@@ -139,6 +159,7 @@ __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, co
     constexpr int NC = kTileRows * CPR / 256;
     static_assert(NC * 256 == kTileRows * CPR, "whole 16-byte chunks per thread");
     Chunk<T> kv[NC], vv[NC], qv[NC];
+    RopeIn<E / 2> rin[ROPE ? NC : 1];
 #pragma unroll
     for (int it = 0; it < NC; ++it) {
         const int c = tid + it * 256;
@@ -148,6 +169,7 @@ __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, co
         kv[it].u = *reinterpret_cast<const uint4*>(k + src);
         vv[it].u = *reinterpret_cast<const uint4*>(v + src);
         if constexpr (NORM || ROPE) qv[it].u = *reinterpret_cast<const uint4*>(q + src);
+        if constexpr (ROPE) rin[it] = RopeIn<E / 2>(rope, pos + 3 * t, (c % CPR) * E / 2);
     }
     // consumed here, so that no load is sunk into the conditional stores below
     // (it would then wait for the one before it)
@@ -157,6 +179,11 @@ __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, co
         asm volatile("" ::"v"(vv[it].u.x), "v"(vv[it].u.y), "v"(vv[it].u.z), "v"(vv[it].u.w));
         if constexpr (NORM || ROPE)
             asm volatile("" ::"v"(qv[it].u.x), "v"(qv[it].u.y), "v"(qv[it].u.z), "v"(qv[it].u.w));
+        if constexpr (ROPE) {
+            asm volatile("" ::"v"(rin[it].pos[0]), "v"(rin[it].pos[1]), "v"(rin[it].pos[2]));
+#pragma unroll
+            for (int j = 0; j < E / 2; ++j) asm volatile("" ::"v"(rin[it].freq[j]));
+        }
     }
 #pragma unroll
     for (int it = 0; it < NC; ++it) {
@@ -177,16 +204,14 @@ __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, co
             }
             row_layer_norm<CPR, E>(qf, norm.w + ch * E, norm.w + D + ch * E, norm.eps);
             row_layer_norm<CPR, E>(kf, norm.w + 2 * D + ch * E, norm.w + 3 * D + ch * E, norm.eps);
-            if constexpr (ROPE) rope_pairs2<E>(kf, qf, rope, pos + 3 * t, ch * E / 2);
+            if constexpr (ROPE) rope_pairs2<E>(kf, qf, rope, rin[it], ch * E / 2);
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 kv[it].e[e] = Elt<T>::st(kf[e]);
                 qv[it].e[e] = Elt<T>::st(qf[e]);
             }
         } else if constexpr (ROPE) {
-            const int32_t* p3 = pos + 3 * t;
-            rope_chunk<T>(kv[it].e, rope, p3, ch * E / 2);
-            rope_chunk<T>(qv[it].e, rope, p3, ch * E / 2);
+            rope_chunk2<T>(kv[it].e, qv[it].e, rope, rin[it], ch * E / 2);
         }
         if (ok) {
             if constexpr (NORM || ROPE) *reinterpret_cast<uint4*>(q + src) = qv[it].u;
@@ -262,18 +287,15 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ q, T* __restr
     for (int64_t c = blockIdx.x * 256ll + threadIdx.x; c < n; c += static_cast<int64_t>(gridDim.x) * 256) {
         const int ch = static_cast<int>(c % CPR);
         const int tok = static_cast<int>(c / (CPR * H));
-        const int32_t* p3 = pos + 3 * tok;
-        Chunk<T> x;
-        if (q != nullptr) {
-            x.u = *reinterpret_cast<const uint4*>(q + c * E);
-            rope_chunk<T>(x.e, rope, p3, ch * E / 2);
-            *reinterpret_cast<uint4*>(q + c * E) = x.u;
-        }
-        if (k != nullptr) {
-            x.u = *reinterpret_cast<const uint4*>(k + c * E);
-            rope_chunk<T>(x.e, rope, p3, ch * E / 2);
-            *reinterpret_cast<uint4*>(k + c * E) = x.u;
-        }
+        // both loads before any use, so they are in flight together (a
+        // missing tensor is rotated as garbage and not stored)
+        Chunk<T> xq, xk;
+        if (q != nullptr) xq.u = *reinterpret_cast<const uint4*>(q + c * E);
+        if (k != nullptr) xk.u = *reinterpret_cast<const uint4*>(k + c * E);
+        const RopeIn<E / 2> in(rope, pos + 3 * tok, ch * E / 2);
+        rope_chunk2<T>(xk.e, xq.e, rope, in, ch * E / 2);
+        if (q != nullptr) *reinterpret_cast<uint4*>(q + c * E) = xq.u;
+        if (k != nullptr) *reinterpret_cast<uint4*>(k + c * E) = xk.u;
     }
 }
 
