@@ -514,6 +514,20 @@ __device__ __forceinline__ void ring_round(int it, int ntiles, Cursor (&cq)[NB],
     }
 }
 
+// Token decode: the new token's key row and V^T column of buffer h into
+// row p.dslot (the cache region is the kernel's own buffer: writable).
+template <int D, int NW>
+__device__ __forceinline__ void decode_token_write(const AttnParams& p, int h, int tid) {
+    const uint16_t* k = static_cast<const uint16_t*>(p.dk) + static_cast<size_t>(h) * D;
+    const uint16_t* v = static_cast<const uint16_t*>(p.dv) + static_cast<size_t>(h) * D;
+    uint16_t* kr = static_cast<uint16_t*>(const_cast<void*>(p.kreg)) + (static_cast<size_t>(h) * p.rows + p.dslot) * D;
+    uint16_t* vr = static_cast<uint16_t*>(const_cast<void*>(p.vreg)) + static_cast<size_t>(h) * D * p.rows + vt_pos(p.dslot);
+    for (int d = tid; d < D; d += NW * 64) {
+        kr[d] = k[d];
+        vr[static_cast<size_t>(d) * p.rows] = v[d];
+    }
+}
+
 // One work item: query tile `qt` of (frame, head h) against key tiles
 // [t_begin, t_end) of the segment list, finished by write_out(piece).
 template <int D, int NW, int QB, bool PREFILL, bool IND = false>
@@ -533,6 +547,16 @@ __device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<P
     const uint16_t* kh = static_cast<const uint16_t*>(p.kreg) + static_cast<size_t>(h) * p.rows * D;
     const uint16_t* vh = static_cast<const uint16_t*>(p.vreg) + static_cast<size_t>(h) * D * p.rows;
     const TileOffsets<D, NW> off(p.rows, wave, lane);
+
+    if constexpr (!PREFILL) {
+        // token decode: the one work item whose range holds the new slot's
+        // tile (the buffer's single segment starts at row 0) writes the new
+        // token first; its stores complete before the tile loads below
+        if (p.dk != nullptr && p.dslot / KT >= t_begin && p.dslot / KT < t_end) {
+            decode_token_write<D, NW>(p, h, tid);
+            sync_tiles<0>();
+        }
+    }
 
     // prologue: tiles 0 .. NB-2 in flight
     Cursor cq[NB];

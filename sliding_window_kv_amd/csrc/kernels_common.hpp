@@ -110,6 +110,11 @@ struct AttnParams {
     int fP;                  // key rows per frame in the region
     SegList seg;             // streaming only
     const SegList* dseg;     // streaming: the segments in device memory instead of seg (captured steps)
+    // token decode: the new token's key and value ([H][D] each), written
+    // into row dslot of their buffer by the work-group that reads its tile
+    const void* dk;
+    const void* dv;
+    int dslot;
 };
 
 }  // namespace swa

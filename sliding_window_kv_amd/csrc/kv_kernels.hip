@@ -329,20 +329,6 @@ __global__ __launch_bounds__(256) void qknorm_kernel(T* __restrict__ q, T* __res
     }
 }
 
-// Token decode append: row `slot` of every (sequence, kv head) rolling
-// buffer gets the new token's key (K row) and value (V^T column, at
-// vt_pos(slot)).  One block of D threads per (sequence, kv head).
-template <int D>
-__global__ __launch_bounds__(64) void decode_append_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                                                           uint16_t* __restrict__ kreg, uint16_t* __restrict__ vreg,
-                                                           int rows, int slot) {
-    const int h = blockIdx.x;
-    for (int d = threadIdx.x; d < D; d += 64) {
-        kreg[(static_cast<size_t>(h) * rows + slot) * D + d] = k[static_cast<size_t>(h) * D + d];
-        vreg[(static_cast<size_t>(h) * D + d) * rows + vt_pos(slot)] = v[static_cast<size_t>(h) * D + d];
-    }
-}
-
 // Visible-page list from the device frame tables and the ring counters:
 // scale frames, retained special entries (oldest first), window frames,
 // pending non-keyframe.
@@ -466,19 +452,6 @@ __global__ __launch_bounds__(64) void plan_store_kernel(StepPlan plan, StepPlan*
 
 hipError_t launch_plan_store(const StepPlan& plan, StepPlan* dst, hipStream_t stream) {
     hipLaunchKernelGGL(plan_store_kernel, dim3(1), dim3(64), 0, stream, plan, dst);
-    return hipGetLastError();
-}
-
-hipError_t launch_decode_append(int D, int nh, int rows, int slot, const void* k, const void* v, void* kreg,
-                                void* vreg, hipStream_t stream) {
-    if (D == 64)
-        hipLaunchKernelGGL((decode_append_kernel<64>), dim3(nh), dim3(64), 0, stream, static_cast<const uint16_t*>(k),
-                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(kreg), static_cast<uint16_t*>(vreg),
-                           rows, slot);
-    else
-        hipLaunchKernelGGL((decode_append_kernel<32>), dim3(nh), dim3(64), 0, stream, static_cast<const uint16_t*>(k),
-                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(kreg), static_cast<uint16_t*>(vreg),
-                           rows, slot);
     return hipGetLastError();
 }
 

@@ -87,14 +87,12 @@ hipError_t launch_merge(int D, int H, int nq, int n, int ncols, const float* par
 
 // Token decode over rolling buffers ([H = sequences x kv heads][rows][D] and
 // V^T): the streaming attention kernel with one wave per work-group, whose
-// 32 query rows are the query heads of one kv group (p.nq <= 32).
+// 32 query rows are the query heads of one kv group (p.nq <= 32).  With
+// p.dk != null the new token (p.dk, p.dv: [H][D]) is written into row
+// p.dslot of every buffer by the work-group that reads that row's tile,
+// before its tile loads.
 hipError_t launch_attention_decode(int D, const AttnParams& p, int grid, hipStream_t stream);
 int attention_decode_blocks_per_cu(int D);
 int attention_decode_q_rows();
-
-// Write each of the nh (sequence, kv head) rows of k, v ([nh][D]) into row
-// `slot` of K ([nh][rows][D]) and V^T ([nh][D][rows], at vt_pos(slot)).
-hipError_t launch_decode_append(int D, int nh, int rows, int slot, const void* k, const void* v, void* kreg,
-                                void* vreg, hipStream_t stream);
 
 }  // namespace swa

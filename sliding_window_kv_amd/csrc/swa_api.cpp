@@ -668,8 +668,6 @@ int swa_decode_step(void* cache, size_t cache_bytes, int B, int Hq, int Hkv, int
     void* kreg = cache;
     void* vreg = static_cast<char*>(cache) + dl.k_bytes;
     const int slot = static_cast<int>(pos % W);
-    hipError_t e = swa::launch_decode_append(D, nh, static_cast<int>(dl.rows), slot, k, v, kreg, vreg, stream);
-    if (e != hipSuccess) return hip_fail(e, "decode append kernel launch");
 
     const int n = static_cast<int>(std::min<int64_t>(pos + 1, W));   // live slots 0..n-1
     swa::AttnParams p{};
@@ -700,9 +698,12 @@ int swa_decode_step(void* cache, size_t cache_bytes, int B, int Hq, int Hkv, int
     cols = std::max<int64_t>(1, std::min<int64_t>(cols, int64_t(nh) * tiles));
     p.ncols = static_cast<int>(cols);
     const int64_t pieces = 2 * int64_t(kMaxDecodeCols);
+    p.dk = k;                                   // the new token goes in with the attention launch
+    p.dv = v;
+    p.dslot = slot;
     p.part_o = static_cast<float*>(work);
     p.part_ml = reinterpret_cast<float*>(static_cast<char*>(work) + align_up(pieces * G * D * 4, 256));
-    e = swa::launch_attention_decode(D, p, p.ncols, stream);
+    hipError_t e = swa::launch_attention_decode(D, p, p.ncols, stream);
     if (e != hipSuccess) return hip_fail(e, "decode attention kernel launch");
     if (!(p.ncols <= nh && nh % p.ncols == 0)) {
         e = swa::launch_merge(D, nh, G, tiles, p.ncols, p.part_o, p.part_ml, out, lse, p.rs, p.hs, nullptr, stream);
