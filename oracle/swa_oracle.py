@@ -20,7 +20,7 @@ against the pages:
   streaming branch (keyframe: append, evict, attend; non-keyframe: append with
   eviction deferred, attend, roll back).
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   frames are bidirectional inside and causal across; num_frame_per_block only
   scales the window; scale frames are visible to every later frame; the
   cache's window counts frames; window -1 means no window; softmax scale is
