@@ -546,7 +546,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("this build runs on one GPU only: use --gpus 1 (the head-sharded multi-GPU layout is design only)",
+        print("bench.py measures one GPU: use --gpus 1 (a multi-GPU, head-sharded layout is not implemented)",
               file=sys.stderr)
         sys.exit(2)
     import torch
