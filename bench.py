@@ -205,7 +205,6 @@ def bench_stream(args, torch, swa):
 
 def bench_prefill(args, torch, swa):
     import numpy as np
-    from oracle import frame_visibility, masked_attention
     from swa_synth import chunk_qkv
     F, P, H, D, W, S = 32, 1374, 16, 64, 8, 8
     qn, kn, vn = chunk_qkv(3, F, P, H, D)
@@ -213,8 +212,8 @@ def bench_prefill(args, torch, swa):
     out = torch.empty_like(q)
     need = swa.swa_prefill_workspace_bytes(F, P, H, D, swa.SWA_BF16)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    vis = frame_visibility(F, W, 1, S)
-    pairs = int(vis.sum())
+    # visible (query frame, key frame) pairs: j <= i and (j >= i - W + 1 or j < S)
+    pairs = sum(1 for i in range(F) for j in range(i + 1) if j >= i - W + 1 or j < S)
     flops = 4.0 * D * H * P * P * pairs
     for _ in range(args.warmup):
         swa.prefill_t(q, k, v, F, P, W, 1, S, out, None, ws)
@@ -227,6 +226,9 @@ def bench_prefill(args, torch, swa):
     res["chunk_layout_bytes"] = 2 * 2 * F * P * H * D * 2
     if not args.no_cpu:
         # oracle rows of query frames 0, 16 and 31 (1, 16 and 16 visible frames)
+        from oracle import frame_visibility, masked_attention
+        vis = frame_visibility(F, W, 1, S)
+        assert int(vis.sum()) == pairs
         fk = np.arange(F * P) // P
         t0 = time.perf_counter()
         sample_pairs = 0
