@@ -270,3 +270,14 @@ def test_graph_argument_checks():
         swa.swa_graph_step(None, 0, 1)
     assert e.value.code == swa.SWA_E_INVAL
     swa.swa_cache_destroy(d)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    # no fallback of any kind: without the built library every entry point
+    # refuses to run
+    monkeypatch.setattr(swa, "LIB_PATH", str(tmp_path / "libswa.so"))
+    monkeypatch.setattr(swa, "_lib", None)
+    with pytest.raises(ImportError):
+        swa.lib()
+    with pytest.raises(ImportError):
+        swa.swa_cache_pool_bytes(swa.make_config(21, 2, 32, sliding_window_size=2))
