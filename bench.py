@@ -91,7 +91,9 @@ def _cores():
     return len(os.sched_getaffinity(0))
 
 
-KERNEL_SOURCES = ("sliding_window_kv_amd/csrc/attn_kernels.hip", "sliding_window_kv_amd/csrc/kernels_common.hpp")
+# the attention kernel's sources and the build script that holds its compile flags
+KERNEL_SOURCES = ("sliding_window_kv_amd/csrc/attn_kernels.hip", "sliding_window_kv_amd/csrc/kernels_common.hpp",
+                  "sliding_window_kv_amd/build.py")
 TRAFFIC_SUMMARY = "profiles/attention_stream_traffic.txt"
 
 

@@ -22,11 +22,16 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
+# The attention kernel alternates matrix products with a vector-ALU softmax;
+# LLVM's max-ILP scheduling strategy interleaves them better than the default
+# occupancy-driven one (same 3 waves per SIMD, no spills; the attention call
+# of the 1374-token, 16-head, 24-frame streaming step measured 1.3% faster).
+PER_SOURCE_FLAGS = {"attn_kernels.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + COMMON + DEVICE_FLAGS
+    cmd = [HIPCC] + COMMON + DEVICE_FLAGS + PER_SOURCE_FLAGS.get(src, [])
     if src.endswith(".hip"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
