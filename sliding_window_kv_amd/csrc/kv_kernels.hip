@@ -136,10 +136,18 @@ __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, co
                                                      T* __restrict__ q, const int32_t* __restrict__ pos,
                                                      RopeArgs rope, NormArgs norm, int H, int n_tok, int row0,
                                                      int rows, int32_t* meta_slot, int32_t frame_id,
-                                                     const StepPlan* __restrict__ plan) {
+                                                     RetainArgs ret, const StepPlan* __restrict__ plan) {
     constexpr int E = Elt<T>::kPer16B;
-    if (plan != nullptr) {                   // captured step: destination and frame id from the device plan
+    if (plan != nullptr) {                   // captured step: destination, ids and retention from the device plan
         row0 = plan->row0;
+        if (ret.ns > 0 && plan->retain != 0) {
+            ret.src_row = plan->retain_src;
+            ret.dst_row = plan->retain_dst;
+            ret.meta = meta_slot + plan->retain_meta;
+            ret.frame = plan->victim_frame;
+        } else {
+            ret.ns = 0;
+        }
         meta_slot += plan->append_meta;
         frame_id = plan->frame;
     }
@@ -152,6 +160,32 @@ __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, co
     const int tid = threadIdx.x;
 
     if (meta_slot != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *meta_slot = frame_id;
+
+    // Retention of the previous occupant's special rows: the block whose
+    // rows hold some of them copies those (K rows, and their V^T columns,
+    // which vt_pos keeps inside the same 16-row group) to the special ring,
+    // and only then overwrites them.
+    {
+        const int lo = ret.src_row > base ? ret.src_row : base;
+        const int hi = ret.src_row + ret.ns < base + kTileRows ? ret.src_row + ret.ns : base + kTileRows;
+        if (lo < hi) {                       // uniform over the block
+            if (ret.meta != nullptr && lo == ret.src_row && h == 0 && tid == 0) *ret.meta = ret.frame;
+            const int nr = hi - lo;
+            const int shift = ret.dst_row - ret.src_row;
+            T* kh = kreg + static_cast<size_t>(h) * rows * D;
+            for (int i = tid; i < nr * D; i += 256) {
+                const int r = lo + i / D;
+                kh[static_cast<size_t>(r + shift) * D + i % D] = kh[static_cast<size_t>(r) * D + i % D];
+            }
+            T* vh = vreg + static_cast<size_t>(h) * D * rows;
+            for (int i = tid; i < nr * D; i += 256) {
+                const int d = i / nr;
+                const int r = lo + i % nr;
+                vh[static_cast<size_t>(d) * rows + vt_pos(r + shift)] = vh[static_cast<size_t>(d) * rows + vt_pos(r)];
+            }
+            __syncthreads();                 // every old row read before any is overwritten
+        }
+    }
 
     // Every thread's loads first, all in flight together; rows outside the
     // frame read token 0 and store nothing (every lane also takes part in
@@ -250,30 +284,6 @@ __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, co
             for (int e = 0; e < E; ++e)
                 if (valid[e]) dst[e] = out.e[e];
         }
-    }
-}
-
-template <typename T, int D>
-__global__ __launch_bounds__(256) void retain_kernel(T* __restrict__ kreg, T* __restrict__ vreg, int rows,
-                                                     int src_row, int dst_row, int ns, int32_t* meta_slot,
-                                                     int32_t frame_id, const StepPlan* __restrict__ plan) {
-    if (plan != nullptr) {                   // captured step: the copy, if any, from the device plan
-        if (plan->retain == 0) return;
-        src_row = plan->retain_src;
-        dst_row = plan->retain_dst;
-        meta_slot += plan->retain_meta;
-        frame_id = plan->victim_frame;
-    }
-    const int h = blockIdx.x;
-    if (meta_slot != nullptr && h == 0 && threadIdx.x == 0) *meta_slot = frame_id;
-    T* kh = kreg + static_cast<size_t>(h) * rows * D;
-    for (int i = threadIdx.x; i < ns * D; i += blockDim.x)
-        kh[static_cast<size_t>(dst_row) * D + i] = kh[static_cast<size_t>(src_row) * D + i];
-    T* vh = vreg + static_cast<size_t>(h) * D * rows;
-    for (int i = threadIdx.x; i < ns * D; i += blockDim.x) {
-        const int d = i / ns;
-        const int r = i % ns;
-        vh[static_cast<size_t>(d) * rows + vt_pos(dst_row + r)] = vh[static_cast<size_t>(d) * rows + vt_pos(src_row + r)];
     }
 }
 
@@ -390,8 +400,8 @@ __global__ __launch_bounds__(256) void mask_kernel(int F, int P, int W, int S, i
 template <typename T, int D>
 hipError_t append_dispatch(int H, int n_tok, int row0, int rows, const void* k, const void* v,
                            void* kreg, void* vreg, void* q, const int32_t* pos, const RopeArgs* rope,
-                           const NormArgs* norm, int32_t* meta_slot, int32_t frame_id, const StepPlan* plan,
-                           hipStream_t stream) {
+                           const NormArgs* norm, int32_t* meta_slot, int32_t frame_id, const RetainArgs& ret,
+                           const StepPlan* plan, hipStream_t stream) {
     const int first = row0 & ~15;
     // with a device plan the first row is not known here: enough tiles for any 16-row offset
     const int tiles = plan != nullptr ? (15 + n_tok + kTileRows - 1) / kTileRows
@@ -404,7 +414,7 @@ hipError_t append_dispatch(int H, int n_tok, int row0, int rows, const void* k, 
 #define SWA_APPEND(RO, NO)                                                                                  \
     hipLaunchKernelGGL((append_kernel<T, D, RO, NO>), grid, dim3(256), 0, stream, static_cast<const T*>(k),  \
                        static_cast<const T*>(v), static_cast<T*>(kreg), static_cast<T*>(vreg), static_cast<T*>(q), \
-                       pos, r, nm, H, n_tok, row0, rows, meta_slot, frame_id, plan)
+                       pos, r, nm, H, n_tok, row0, rows, meta_slot, frame_id, ret, plan)
     if (rope != nullptr && norm != nullptr)
         SWA_APPEND(true, true);
     else if (rope != nullptr)
@@ -422,19 +432,19 @@ hipError_t append_dispatch(int H, int n_tok, int row0, int rows, const void* k, 
 hipError_t launch_append(int dtype, int H, int D, int n_tok, int row0, int rows, const void* k,
                          const void* v, void* kreg, void* vreg, void* q, const int32_t* pos,
                          const RopeArgs* rope, const NormArgs* norm, int32_t* meta_slot, int32_t frame_id,
-                         const StepPlan* plan, hipStream_t stream) {
+                         const RetainArgs& ret, const StepPlan* plan, hipStream_t stream) {
     if (dtype == 0) {
         if (D == 64)
             return append_dispatch<uint16_t, 64>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm,
-                                                 meta_slot, frame_id, plan, stream);
+                                                 meta_slot, frame_id, ret, plan, stream);
         return append_dispatch<uint16_t, 32>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm,
-                                             meta_slot, frame_id, plan, stream);
+                                             meta_slot, frame_id, ret, plan, stream);
     }
     if (D == 64)
         return append_dispatch<float, 64>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm, meta_slot,
-                                          frame_id, plan, stream);
+                                          frame_id, ret, plan, stream);
     return append_dispatch<float, 32>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm, meta_slot,
-                                      frame_id, plan, stream);
+                                      frame_id, ret, plan, stream);
 }
 
 namespace {
@@ -474,31 +484,6 @@ hipError_t launch_qknorm(int dtype, int n_tok, int H, int D, void* q, void* k, c
         else
             hipLaunchKernelGGL((qknorm_kernel<float, 32>), dim3(blocks), dim3(256), 0, stream,
                                static_cast<float*>(q), static_cast<float*>(k), norm, n);
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_retain(int dtype, int H, int D, int rows, int src_row, int dst_row, int ns,
-                         void* kreg, void* vreg, int32_t* meta_slot, int32_t frame_id, const StepPlan* plan,
-                         hipStream_t stream) {
-    if (dtype == 0) {
-        if (D == 64)
-            hipLaunchKernelGGL((retain_kernel<uint16_t, 64>), dim3(H), dim3(256), 0, stream,
-                               static_cast<uint16_t*>(kreg), static_cast<uint16_t*>(vreg), rows, src_row,
-                               dst_row, ns, meta_slot, frame_id, plan);
-        else
-            hipLaunchKernelGGL((retain_kernel<uint16_t, 32>), dim3(H), dim3(256), 0, stream,
-                               static_cast<uint16_t*>(kreg), static_cast<uint16_t*>(vreg), rows, src_row,
-                               dst_row, ns, meta_slot, frame_id, plan);
-    } else {
-        if (D == 64)
-            hipLaunchKernelGGL((retain_kernel<float, 64>), dim3(H), dim3(256), 0, stream,
-                               static_cast<float*>(kreg), static_cast<float*>(vreg), rows, src_row, dst_row,
-                               ns, meta_slot, frame_id, plan);
-        else
-            hipLaunchKernelGGL((retain_kernel<float, 32>), dim3(H), dim3(256), 0, stream,
-                               static_cast<float*>(kreg), static_cast<float*>(vreg), rows, src_row, dst_row,
-                               ns, meta_slot, frame_id, plan);
     }
     return hipGetLastError();
 }

@@ -21,6 +21,17 @@ struct NormArgs {
     float eps;
 };
 
+// Special-row retention fused into an append: before the frame overwrites
+// its slot, the ns rows starting at src_row of every head (K and V^T) are
+// copied to dst_row, and meta, if not null, receives frame.  ns = 0: no copy.
+// With a device plan (captured steps) the copy happens only if plan->retain,
+// with rows, id and metadata entry (meta + plan->retain_meta) from the plan.
+struct RetainArgs {
+    int src_row, dst_row, ns;
+    int32_t* meta;
+    int32_t frame;
+};
+
 // Copy n_tok tokens of k, v ([n_tok, H, D]) into rows [row0, row0 + n_tok)
 // of the K region ([H][rows][D]) and the transposed V region ([H][D][rows]).
 // With norm != null, k is layer-normed per head on the way and q
@@ -28,10 +39,12 @@ struct NormArgs {
 // in place (after the norm).  meta_slot, if not null, receives frame_id.
 // With plan != null (captured steps) row0, frame_id and the metadata entry
 // (meta_slot + plan->append_meta) are read from the device plan instead.
+// `ret` is the retention of the special rows of the slot's previous
+// occupant, done by the same launch before its rows are overwritten.
 hipError_t launch_append(int dtype, int H, int D, int n_tok, int row0, int rows, const void* k,
                          const void* v, void* kreg, void* vreg, void* q, const int32_t* pos,
                          const RopeArgs* rope, const NormArgs* norm, int32_t* meta_slot, int32_t frame_id,
-                         const StepPlan* plan, hipStream_t stream);
+                         const RetainArgs& ret, const StepPlan* plan, hipStream_t stream);
 
 // Store one step's ring plan into device memory (read by the kernels of a
 // captured step).
@@ -39,14 +52,6 @@ hipError_t launch_plan_store(const StepPlan& plan, StepPlan* dst, hipStream_t st
 
 // Per-head layer norm of q and/or k ([n_tok, H, D]) in place.
 hipError_t launch_qknorm(int dtype, int n_tok, int H, int D, void* q, void* k, const NormArgs& norm,
-                         hipStream_t stream);
-
-// Copy `ns` rows starting at src_row of every head (K and V^T) to dst_row;
-// meta_slot, if not null, receives frame_id.  With plan != null the copy
-// happens only if plan->retain, with rows, id and metadata entry
-// (meta_slot + plan->retain_meta) from the device plan.
-hipError_t launch_retain(int dtype, int H, int D, int rows, int src_row, int dst_row, int ns,
-                         void* kreg, void* vreg, int32_t* meta_slot, int32_t frame_id, const StepPlan* plan,
                          hipStream_t stream);
 
 hipError_t launch_rope(int dtype, int n_tok, int H, int D, void* q, void* k, const int32_t* pos,

@@ -201,25 +201,26 @@ int pick_columns(const swa_cache* c, int qtiles, int n) {
     return static_cast<int>(std::max<int64_t>(cols, 1));
 }
 
-// Enqueue the device side of one append (special-row retention first, then
-// the frame copy with optional RoPE).
+// Enqueue the device side of one append: one launch that retains the special
+// rows of the slot's previous occupant (if it is evicted) and then copies the
+// frame in, with optional norm and RoPE.
 int enqueue_append(swa_cache* c, int layer, const swa::AppendPlan& plan, int64_t t, void* q,
                    const void* k, const void* v, const int32_t* pos, const swa::NormArgs* norm,
                    hipStream_t stream) {
     const Layout& L = c->L;
     const int dt = c->cfg.dtype;
-    if (plan.retain) {
-        const int src = plan.victim_slot * L.P + c->cfg.special_row0;
-        const int dst = L.special_row_base + plan.special_slot * L.ns;
-        hipError_t e = swa::launch_retain(dt, L.H, L.D, L.rows, src, dst, L.ns, c->kreg(layer), c->vreg(layer),
-                                          c->meta(layer) + L.meta_special + plan.special_id_index,
-                                          static_cast<int32_t>(plan.victim_frame), nullptr, stream);
-        if (e != hipSuccess) return hip_fail(e, "retain kernel launch");
+    swa::RetainArgs ret{0, 0, 0, nullptr, 0};
+    if (plan.retain) {                       // the slot's occupant is evicted: its special rows go first
+        ret.src_row = plan.victim_slot * L.P + c->cfg.special_row0;
+        ret.dst_row = L.special_row_base + plan.special_slot * L.ns;
+        ret.ns = L.ns;
+        ret.meta = c->meta(layer) + L.meta_special + plan.special_id_index;
+        ret.frame = static_cast<int32_t>(plan.victim_frame);
     }
     int32_t* slot_meta = plan.keyframe ? c->meta(layer) + plan.ord_index : c->meta(layer) + L.meta_pending;
     hipError_t e = swa::launch_append(dt, L.H, L.D, L.P, plan.slot * L.P, L.rows, k, v, c->kreg(layer),
                                       c->vreg(layer), q, pos, pos != nullptr ? &c->rope : nullptr, norm, slot_meta,
-                                      static_cast<int32_t>(t), nullptr, stream);
+                                      static_cast<int32_t>(t), ret, nullptr, stream);
     if (e != hipSuccess) return hip_fail(e, "append kernel launch");
     return SWA_OK;
 }
@@ -294,22 +295,18 @@ int enqueue_attention(swa_cache* c, int layer, const void* q, void* out, float* 
 }
 
 // One layer's step with every ring-dependent value read from the device
-// step plan, for capture: retain (a no-op unless the plan asks), append
-// (+ norm, + RoPE), attention over the plan's segments on a fixed number of
+// step plan, for capture: append (+ retention if the plan asks, + norm,
+// + RoPE), attention over the plan's segments on a fixed number of
 // columns, merge.
 int enqueue_planned_layer(swa_cache* c, int layer, void* q, const void* k, const void* v, const int32_t* pos,
                           const swa::NormArgs* norm, void* out, float* lse, hipStream_t stream) {
     const Layout& L = c->L;
     const int dt = c->cfg.dtype;
     const swa::StepPlan* plan = c->step_plan();
-    hipError_t e;
-    if (c->cfg.cross_frame_special) {
-        e = swa::launch_retain(dt, L.H, L.D, L.rows, 0, 0, L.ns, c->kreg(layer), c->vreg(layer), c->meta(layer), 0,
-                               plan, stream);
-        if (e != hipSuccess) return hip_fail(e, "retain kernel launch");
-    }
-    e = swa::launch_append(dt, L.H, L.D, L.P, 0, L.rows, k, v, c->kreg(layer), c->vreg(layer), q, pos,
-                           pos != nullptr ? &c->rope : nullptr, norm, c->meta(layer), 0, plan, stream);
+    // retention (if the plan asks) happens inside the append
+    const swa::RetainArgs ret{0, 0, c->cfg.cross_frame_special ? L.ns : 0, nullptr, 0};
+    hipError_t e = swa::launch_append(dt, L.H, L.D, L.P, 0, L.rows, k, v, c->kreg(layer), c->vreg(layer), q, pos,
+                                      pos != nullptr ? &c->rope : nullptr, norm, c->meta(layer), 0, ret, plan, stream);
     if (e != hipSuccess) return hip_fail(e, "append kernel launch");
     swa::AttnParams p = frame_attn_params(c, layer, q, out, lse);
     p.dseg = &plan->seg;
@@ -737,7 +734,7 @@ int swa_prefill_masked(const void* q, const void* k, const void* v, int F, int P
     void* vreg = static_cast<char*>(ws) + need / 2;
     // the F frames laid out as consecutive pages (frame f in rows [f*P, (f+1)*P))
     hipError_t e = swa::launch_append(dtype, H, D, F * P, 0, rows, k, v, kreg, vreg, nullptr, nullptr, nullptr, nullptr,
-                                      nullptr, 0, nullptr, stream);
+                                      nullptr, 0, swa::RetainArgs{0, 0, 0, nullptr, 0}, nullptr, stream);
     if (e != hipSuccess) return hip_fail(e, "chunk layout kernel launch");
     swa::AttnParams p{};
     p.q = q;

@@ -16,15 +16,12 @@ namespace {
 }  // namespace
 
 hipError_t launch_append(int, int, int, int, int, int, const void*, const void*, void*, void*, void*, const int32_t*,
-                         const RopeArgs*, const NormArgs*, int32_t*, int32_t, const StepPlan*, hipStream_t) {
+                         const RopeArgs*, const NormArgs*, int32_t*, int32_t, const RetainArgs&, const StepPlan*,
+                         hipStream_t) {
     no_device("launch_append");
 }
 hipError_t launch_plan_store(const StepPlan&, StepPlan*, hipStream_t) { no_device("launch_plan_store"); }
 hipError_t launch_qknorm(int, int, int, int, void*, void*, const NormArgs&, hipStream_t) { no_device("launch_qknorm"); }
-hipError_t launch_retain(int, int, int, int, int, int, int, void*, void*, int32_t*, int32_t, const StepPlan*,
-                         hipStream_t) {
-    no_device("launch_retain");
-}
 hipError_t launch_rope(int, int, int, int, void*, void*, const int32_t*, const RopeArgs&, hipStream_t) {
     no_device("launch_rope");
 }
