@@ -30,9 +30,9 @@ def _oracle_step(oc, t, q, k, v, keyframe, rows):
 
 
 def _run(P, H, D, W, S, L, T, keyframe_of=lambda t: True, cross=False, ns=5, R=1000, rope=(0, 0, 0),
-         grid=None, norm=False, rows=None, oracle_at=None, splits=None):
+         grid=None, norm=False, rows=None, oracle_at=None, splits=None, sr0=0):
     cfg = swa.make_config(P, H, D, sliding_window_size=W, scale_frames=S, num_layers=L, cross_frame_special=cross,
-                          special_rows=ns, max_special_frames=R, rope=rope)
+                          special_row0=sr0, special_rows=ns, max_special_frames=R, rope=rope)
     gcache, ecache = swa.SwaCache(cfg), swa.SwaCache(cfg)
     if splits is not None:                   # before the capture: the column count is fixed in the graph
         gcache.set_splits(splits)
@@ -47,7 +47,7 @@ def _run(P, H, D, W, S, L, T, keyframe_of=lambda t: True, cross=False, ns=5, R=1
     wds = [torch.from_numpy(w).cuda() for w in ws] if norm else None
     graph = swa.SwaGraph(gcache, qs, ks, vs, outs, lses, pos=posbuf, norm_weights=wds, eps=EPS)
     ocs = [NaiveRingCache(CacheConfig(P=P, sliding_window_size=W, scale_frames=S, cross_frame_special=cross,
-                                      special_rows=ns, max_special_frames=R)) for _ in range(L)]
+                                      special_row0=sr0, special_rows=ns, max_special_frames=R)) for _ in range(L)]
     for t in range(T):
         kf = keyframe_of(t)
         frames = [frame_qkv(200 + l, t, P, H, D) for l in range(L)]
@@ -123,6 +123,13 @@ def test_graph_specials_nonkeyframes_rope_norm():
     case("graph step with retention, non-keyframes, rope and norm")
     _run(105, 2, 64, 3, 2, 2, 20, keyframe_of=lambda t: t % 3 != 2, cross=True, ns=5, R=4,
          rope=(12, 10, 10), grid=(10, 10), norm=True)
+
+
+def test_graph_specials_across_tile_boundaries():
+    # retention read from the device step plan, with the special rows
+    # (60..68) straddling the append's 64-row work-group boundary in slot 0
+    case("graph step with special rows 60..68, no scale frame")
+    _run(150, 2, 64, 2, 0, 2, 12, keyframe_of=lambda t: t % 3 != 2, cross=True, ns=9, R=3, sr0=60)
 
 
 def test_graph_frame_shape_sampled():

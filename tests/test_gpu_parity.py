@@ -18,12 +18,12 @@ pytestmark = pytest.mark.gpu
 
 
 def _cache(P, H, D, dtype, W, S, nfpb=1, cross=False, ns=5, R=1000, max_frames=64, rope=(0, 0, 0),
-           num_layers=1):
+           num_layers=1, sr0=0):
     cfg = swa.make_config(P, H, D, dtype=dtype, sliding_window_size=W, num_frame_per_block=nfpb,
-                          scale_frames=S, cross_frame_special=cross, special_rows=ns, max_special_frames=R,
-                          max_frames=max_frames, rope=rope, num_layers=num_layers)
+                          scale_frames=S, cross_frame_special=cross, special_row0=sr0, special_rows=ns,
+                          max_special_frames=R, max_frames=max_frames, rope=rope, num_layers=num_layers)
     ocfg = CacheConfig(P=P, sliding_window_size=W, num_frame_per_block=nfpb, scale_frames=S,
-                       cross_frame_special=cross, special_row0=0, special_rows=ns, max_special_frames=R,
+                       cross_frame_special=cross, special_row0=sr0, special_rows=ns, max_special_frames=R,
                        max_frames=max_frames)
     return swa.SwaCache(cfg), NaiveRingCache(ocfg)
 
@@ -156,6 +156,42 @@ def test_cache_bytes_bit_exact():
             base = L.special_row_base + row0
             assert np.array_equal(K[:, base:base + nrows, :], k[:nrows].transpose(1, 0, 2))
             assert np.array_equal(V[:, :, base:base + nrows], v[:nrows].transpose(1, 2, 0))
+
+
+def test_specials_across_tile_boundaries():
+    # special rows 60..68 of a frame: in slot 0 they straddle the append's
+    # 64-row work-group boundary (each work-group retains the rows it is
+    # about to overwrite), in slot 1 (rows 210..218) they do not; both
+    # straddle a 16-row V^T group.  No scale frame, so both slots are
+    # reused.  Outputs, pages and the retained bytes against the oracle.
+    P, H, D, W, S, ns, R, sr0 = 150, 2, 64, 2, 0, 9, 3, 60
+    case(f"specials at rows {sr0}..{sr0 + ns - 1}, P={P} W={W} R={R}")
+    gc, oc = _cache(P, H, D, swa.SWA_BF16, W, S, cross=True, ns=ns, R=R, sr0=sr0)
+    frames = {}
+    for t in range(12):
+        kf = t % 3 != 2
+        q, k, v = frame_qkv(8, t, P, H, D)
+        frames[t] = (k, v)
+        qd, kd, vd = dev(q), dev(k), dev(v)
+        out = torch.empty_like(qd)
+        lse = torch.empty((H, P), dtype=torch.float32, device="cuda")
+        gc.step(0, t, qd, kd, vd, kf, out, lse)
+        ro, rl, pages = oc.step(t, q, k, v, kf)
+        assert_close_bf16(host(out), ro, f"out t={t}")
+        assert np.abs(host(lse) - rl).max() <= 1e-2
+        assert gc.pages() == oc.visible_pages()
+    torch.cuda.synchronize()
+    kr, vr = gc.region_views(0)
+    K = kr.float().cpu().numpy()
+    r = np.arange(vr.shape[2])
+    V = vr.float().cpu().numpy()[:, :, (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1)]
+    base = gc.layout.special_row_base
+    specials = [p for p in gc.pages() if p[1] != swa.SWA_REGION_FRAME]
+    assert len(specials) == R
+    for (f, _, _, row0, nrows) in specials:
+        k, v = frames[f]
+        assert np.array_equal(K[:, base + row0:base + row0 + nrows, :], k[sr0:sr0 + nrows].transpose(1, 0, 2))
+        assert np.array_equal(V[:, :, base + row0:base + row0 + nrows], v[sr0:sr0 + nrows].transpose(1, 2, 0))
 
 
 def test_frame_id_closed_form():
