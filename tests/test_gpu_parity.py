@@ -158,6 +158,25 @@ def test_cache_bytes_bit_exact():
             assert np.array_equal(V[:, :, base:base + nrows], v[:nrows].transpose(1, 2, 0))
 
 
+@pytest.mark.parametrize("sr0", [0, 17])
+def test_stream_f32_specials_nonkey(sr0):
+    # fp32 cache: special-row retention inside the fp32 append, non-keyframes
+    P, H, D, W, S, ns, R = 21, 2, 32, 2, 1, 3, 2
+    case(f"stream fp32 specials P={P} W={W} S={S} ns={ns} R={R} rows from {sr0}")
+    gc, oc = _cache(P, H, D, swa.SWA_F32, W, S, cross=True, ns=ns, R=R, sr0=sr0)
+    for t in range(10):
+        kf = t % 3 != 2
+        q, k, v = frame_qkv(9, t, P, H, D, bf16=False)
+        qd, kd, vd = (dev(x, torch.float32) for x in (q, k, v))
+        out = torch.empty_like(qd)
+        lse = torch.empty((H, P), dtype=torch.float32, device="cuda")
+        gc.step(0, t, qd, kd, vd, kf, out, lse)
+        ro, rl, pages = oc.step(t, q, k, v, kf)
+        assert_close_f32(host(out), ro, f"out t={t}")
+        assert_close_f32(host(lse), rl, f"lse t={t}")
+        assert gc.pages() == oc.visible_pages()
+
+
 def test_specials_across_tile_boundaries():
     # special rows 60..68 of a frame: in slot 0 they straddle the append's
     # 64-row work-group boundary (each work-group retains the rows it is
