@@ -83,6 +83,10 @@ enum swa_region { SWA_REGION_FRAME = 0, SWA_REGION_SPECIAL = 1 };
  *                          3-D RoPE bands used by swa_stream_step when a
  *                          position array is given ([IO] "Positional
  *                          Embeddings"); pairs must add up to D/2.
+ * Size limit: one head's K (and V^T) region, rows x D x element bytes with
+ * rows = (page slots x P + R x special_rows) rounded up to 64 plus 64, must
+ * stay below 2 GiB (the kernels address it with 32-bit offsets); larger
+ * configs are rejected with SWA_E_INVAL.
  */
 typedef struct swa_config {
     int32_t num_layers;
@@ -211,15 +215,24 @@ int kvcache_rollback(swa_cache* cache, int layer, swa_stream_t stream);
  * visible row of the layer -- scale frames, retained special rows, window
  * frames and a pending non-keyframe -- with softmax scale 1/sqrt(D).  Writes
  * out (device [P, H, D]) and, if not NULL, lse (device float [H, P]).
- * SWA_E_STATE if nothing is cached. */
+ * SWA_E_STATE if nothing is cached, or if a keyframe append has filled the
+ * window past W frames and kvcache_evict has not run yet: [G] "KV Cache
+ * Eviction Strategy" evicts before attention, and the append has already
+ * overwritten the page of the frame that eviction drops. */
 int kvcache_attend(swa_cache* cache, int layer, const void* q, void* out, float* lse, swa_stream_t stream);
 
 /* Host copy of the layer's visible-page list (records in key order).  Writes
- * min(n, cap) records to `out` and the full count to *n_out. */
+ * min(n, cap) records to `out` and the full count to *n_out.  Between a
+ * keyframe append into a full window and its kvcache_evict the list still
+ * names the frame the eviction will drop, although its page already holds
+ * the new frame (bookkeeping view; kvcache_attend refuses that state). */
 int kvcache_visible_pages(const swa_cache* cache, int layer, swa_page* out, int cap, int* n_out);
 
 /* The same list built on the device from the device-side frame tables (the
- * page-list builder kernel), copied back; synchronises `stream`. */
+ * page-list builder kernel), copied back; synchronises `stream`.  A test
+ * export: the attention kernels take their key rows from the host ring, not
+ * from this list.  SWA_E_STATE while an eviction is pending (see
+ * kvcache_attend) and on a bookkeeping-only cache. */
 int kvcache_read_device_pages(swa_cache* cache, int layer, swa_page* host_out, int cap, int* n_out,
                               swa_stream_t stream);
 
@@ -343,7 +356,8 @@ int swa_graph_destroy(swa_graph* graph);
  * Errors: SWA_E_INVAL for null pointers, sizes < 1, Hq not a multiple of
  *   Hkv, pos < 0, too small or misaligned buffers; SWA_E_UNSUPPORTED for
  *   head_dim other than 32 or 64 or more than 32 query heads per kv head.
- *   The size queries return 0 for invalid arguments.
+ *   The size queries return 0 for invalid arguments, including windows
+ *   whose rows x D x 2 bytes reach 2 GiB per buffer.
  */
 size_t swa_decode_cache_bytes(int B, int Hkv, int W, int D);
 size_t swa_decode_workspace_bytes(int Hq, int Hkv, int D);
@@ -356,9 +370,12 @@ int swa_decode_step(void* cache, size_t cache_bytes, int B, int Hq, int Hkv, int
  * CausalAttention"): query frame i sees key frame j iff j <= i and
  * (j >= i - W + 1 or j < scale_frames), W = sliding_window_size *
  * num_frame_per_block (-1: no window).  q, k, v, out: device [F*P, H, D];
- * lse: device float [H, F*P] or NULL.  bf16 needs a device workspace of
- * swa_prefill_workspace_bytes() bytes (the frames are re-laid out there);
- * F32 needs none (pass NULL, 0).
+ * lse: device float [H, F*P] or NULL.  Both dtypes need a device workspace
+ * of swa_prefill_workspace_bytes() bytes, 256-byte aligned (the frames' keys
+ * and transposed values are laid out there as consecutive pages; contents
+ * need no initialisation).  SWA_E_INVAL (and a size query of 0) when one
+ * head's F*P key rows, rounded up to 64 plus 64, times D times the element
+ * size reach 2 GiB.
  */
 size_t swa_prefill_workspace_bytes(int F, int P, int H, int D, int dtype);
 int swa_prefill_masked(const void* q, const void* k, const void* v, int F, int P, int H, int D,

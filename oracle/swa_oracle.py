@@ -430,7 +430,16 @@ class NaiveRingCache:
         return k, v
 
     def attend(self, q: np.ndarray):
-        """Attention of q [P, H, D] over every cached key (all are visible)."""
+        """Attention of q [P, H, D] over every cached key (all are visible).
+
+        The guide's "KV Cache Eviction Strategy" evicts before attention, so
+        a keyframe appended to a full window must be followed by evict()
+        before attend(): in between, more than window + scale frames are
+        cached and attending is refused.
+        """
+        W, S = self.cfg.W, self.cfg.scale_frames
+        if W is not None and len(self.cached) > S + W:
+            raise RingError("evict before attending")
         k, v = self.keys_values()
         mask = np.ones((q.shape[0], k.shape[0]), dtype=bool)
         return masked_attention(q, k, v, mask)

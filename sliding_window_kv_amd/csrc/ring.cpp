@@ -52,7 +52,7 @@ int Ring::plan_append(int64_t t, bool keyframe, AppendPlan* plan, std::string* e
         *err = "a non-keyframe is pending; roll it back before the next append";
         return SWA_E_STATE;
     }
-    if (cfg_.W >= 0 && n_win_ > cfg_.W) {
+    if (eviction_pending()) {
         *err = "an eviction is pending; call kvcache_evict before the next append";
         return SWA_E_STATE;
     }

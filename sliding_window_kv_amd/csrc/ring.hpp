@@ -78,6 +78,10 @@ public:
     // Row segments of the visible keys in key order, adjacent ones merged.
     void segments(std::vector<RowSeg>* out) const;
     int64_t visible_rows() const;
+    // A keyframe was appended to a full window and the eviction that makes
+    // room for it has not run yet: the append has already overwritten the
+    // page of the frame the eviction drops.
+    bool eviction_pending() const { return cfg_.W >= 0 && n_win_ > cfg_.W; }
 
     RingCounters counters() const;
     int num_slots() const { return num_slots_; }

@@ -41,6 +41,14 @@ struct Layout {
     int64_t part_o_floats;                               // floats of the O partials
 };
 
+// One head's K or V^T region is addressed with 32-bit offsets inside the
+// kernels (feature d of V^T starts d * rows elements in, loads add a byte
+// offset of twice that): keep D * rows * element size below 2^31.
+bool row_space_fits(int64_t used_rows, int D, int elem) {
+    const int64_t rows = (used_rows + 64 + 63) / 64 * 64;
+    return rows * D * elem < (int64_t(1) << 31);
+}
+
 int check_config(const swa_config* c, std::string* err) {
     if (c == nullptr) return *err = "null config", SWA_E_INVAL;
     if (c->num_layers < 1) return *err = "num_layers must be >= 1", SWA_E_INVAL;
@@ -68,6 +76,8 @@ int check_config(const swa_config* c, std::string* err) {
     const int64_t sp = c->cross_frame_special ? static_cast<int64_t>(c->max_special_frames) * c->special_rows : 0;
     if (slots * c->tokens_per_frame + sp + 128 > (1ll << 30) || W > (1 << 24))
         return *err = "cache row space too large", SWA_E_INVAL;
+    if (!row_space_fits(slots * c->tokens_per_frame + sp, c->head_dim, c->dtype == SWA_BF16 ? 2 : 4))
+        return *err = "cache row space too large: one head's region must stay below 2 GiB", SWA_E_INVAL;
     const int pairs = c->rope_pairs_t + c->rope_pairs_h + c->rope_pairs_w;
     if (pairs != 0 && (pairs != c->head_dim / 2 || c->rope_pairs_t < 0 || c->rope_pairs_h < 0 ||
                        c->rope_pairs_w < 0 || !(c->rope_theta > 0.f)))
@@ -446,6 +456,8 @@ int kvcache_rollback(swa_cache* c, int layer, swa_stream_t) {
 int kvcache_attend(swa_cache* c, int layer, const void* q, void* out, float* lse, swa_stream_t stream) {
     const int rc = check_layer(c, layer);
     if (rc != SWA_OK) return rc;
+    if (c->rings[layer].eviction_pending())
+        return fail(SWA_E_STATE, "an eviction is pending; call kvcache_evict before attending");
     if (c->dry) return fail(SWA_E_STATE, "bookkeeping-only cache cannot attend");
     if (q == nullptr || out == nullptr) return fail(SWA_E_INVAL, "null tensor");
     return enqueue_attention(c, layer, q, out, lse, stream);
@@ -473,6 +485,8 @@ int kvcache_read_device_pages(swa_cache* c, int layer, swa_page* host_out, int c
                               swa_stream_t stream) {
     int rc = check_layer(c, layer);
     if (rc != SWA_OK) return rc;
+    if (c->rings[layer].eviction_pending())
+        return fail(SWA_E_STATE, "an eviction is pending; call kvcache_evict before reading the page list");
     if (c->dry) return fail(SWA_E_STATE, "bookkeeping-only cache has no device state");
     if (n_out == nullptr || cap < 0 || (cap > 0 && host_out == nullptr)) return fail(SWA_E_INVAL, "bad output buffer");
     const swa::Ring& ring = c->rings[layer];
@@ -633,7 +647,7 @@ int qk_norm_apply(void* q, void* k, int n_tokens, int H, int D, const float* wei
 
 size_t swa_decode_cache_bytes(int B, int Hkv, int W, int D) {
     if (B < 1 || Hkv < 1 || W < 1 || (D != 32 && D != 64)) return 0;
-    if (int64_t(W) + 128 > (1ll << 30)) return 0;
+    if (int64_t(W) + 128 > (1ll << 30) || !row_space_fits(W, D, 2)) return 0;
     return static_cast<size_t>(decode_layout(B, Hkv, W, D).total);
 }
 
@@ -654,7 +668,7 @@ int swa_decode_step(void* cache, size_t cache_bytes, int B, int Hq, int Hkv, int
     const int G = Hq / Hkv;
     if (G > swa::attention_decode_q_rows()) return fail(SWA_E_UNSUPPORTED, "more than 32 query heads per kv head");
     if (pos < 0) return fail(SWA_E_INVAL, "position must be >= 0");
-    if (int64_t(W) + 128 > (1ll << 30)) return fail(SWA_E_INVAL, "window too large");
+    if (int64_t(W) + 128 > (1ll << 30) || !row_space_fits(W, D, 2)) return fail(SWA_E_INVAL, "window too large");
     const DecodeLayout dl = decode_layout(B, Hkv, W, D);
     if (cache_bytes < static_cast<size_t>(dl.total)) return fail(SWA_E_INVAL, "cache smaller than swa_decode_cache_bytes()");
     if (work_bytes < static_cast<size_t>(decode_work_bytes(G, D)))
@@ -711,6 +725,7 @@ int swa_decode_step(void* cache, size_t cache_bytes, int B, int Hq, int Hkv, int
 
 size_t swa_prefill_workspace_bytes(int F, int P, int H, int D, int dtype) {
     if (F < 1 || P < 1 || H < 1 || (D != 32 && D != 64) || (dtype != SWA_BF16 && dtype != SWA_F32)) return 0;
+    if (int64_t(F) * P + 128 > (1ll << 30) || !row_space_fits(int64_t(F) * P, D, dtype == SWA_BF16 ? 2 : 4)) return 0;
     const int64_t rows = align_up(int64_t(F) * P + 64, 64);
     const int64_t elem = dtype == SWA_BF16 ? 2 : 4;
     return static_cast<size_t>(2 * align_up(int64_t(H) * rows * D * elem, 256));
@@ -724,6 +739,8 @@ int swa_prefill_masked(const void* q, const void* k, const void* v, int F, int P
     if (int64_t(F) * P + 128 > (1ll << 30)) return fail(SWA_E_INVAL, "too many tokens");
     if (D != 32 && D != 64) return fail(SWA_E_UNSUPPORTED, "head_dim must be 32 or 64");
     if (dtype != SWA_BF16 && dtype != SWA_F32) return fail(SWA_E_INVAL, "bad dtype");
+    if (!row_space_fits(int64_t(F) * P, D, dtype == SWA_BF16 ? 2 : 4))
+        return fail(SWA_E_INVAL, "too many tokens: one head's key region must stay below 2 GiB");
     if (sws == 0 || sws < -1 || nfpb < 1 || S < 0) return fail(SWA_E_INVAL, "bad window arguments");
     const size_t need = swa_prefill_workspace_bytes(F, P, H, D, dtype);
     if (ws == nullptr || ws_bytes < need) return fail(SWA_E_INVAL, "workspace smaller than swa_prefill_workspace_bytes()");

@@ -77,6 +77,58 @@ def test_bookkeeping_cache_refuses_device_work():
     assert e.value.code == swa.SWA_E_INVAL
 
 
+def test_attend_refused_while_an_eviction_is_pending():
+    # window 2, 1 scale frame: the 4th keyframe fills the window past 2
+    # frames; until kvcache_evict runs, attending (and reading the device
+    # page list) is refused, as the oracle refuses it
+    ora, h = _pair(5, 2, 1, True, 2, 3)
+    p = ctypes.c_void_p(256)
+    try:
+        for t in range(3):
+            ora.append(t, *_kv(5), True)
+            ora.evict()
+            swa.kvcache_append(h, 0, t, None, None, True)
+            swa.kvcache_evict(h, 0)
+        ora.append(3, *_kv(5), True)
+        swa.kvcache_append(h, 0, 3, None, None, True)
+        with pytest.raises(RingError):
+            ora.attend(np.zeros((5, 1, 1)))
+        for call in (lambda: swa.kvcache_attend(h, 0, p, p, None),
+                     lambda: swa.kvcache_read_device_pages(h, 0, 16)):
+            with pytest.raises(swa.SwaError) as e:
+                call()
+            assert e.value.code == swa.SWA_E_STATE and "eviction is pending" in str(e.value)
+        ora.evict()
+        swa.kvcache_evict(h, 0)
+        ora.attend(np.zeros((5, 1, 1)))
+        with pytest.raises(swa.SwaError) as e:          # now only the missing pool stops it
+            swa.kvcache_attend(h, 0, p, p, None)
+        assert e.value.code == swa.SWA_E_STATE and "bookkeeping-only" in str(e.value)
+        assert swa.kvcache_visible_pages(h, 0) == ora.visible_pages()
+    finally:
+        swa.swa_cache_destroy(h)
+
+
+def test_row_space_limit():
+    # one head's K / V^T region is addressed with 32-bit offsets: rows x D x
+    # element bytes must stay below 2 GiB (window off, 30,000 frames of 1374
+    # tokens at D = 64 would be 5.3 GB per head)
+    big = swa.make_config(1374, 1, 64, sliding_window_size=-1, max_frames=30000)
+    assert swa.swa_cache_pool_bytes(big) == 0
+    with pytest.raises(swa.SwaError) as e:
+        swa.swa_cache_create(big, None, 0)
+    assert e.value.code == swa.SWA_E_INVAL
+    ok = swa.make_config(1374, 1, 64, sliding_window_size=-1, max_frames=12000)   # 2.1e9 B: just under
+    assert swa.swa_cache_pool_bytes(ok) > 0
+    f32 = swa.make_config(1374, 1, 64, dtype=swa.SWA_F32, sliding_window_size=-1, max_frames=12000)
+    assert swa.swa_cache_pool_bytes(f32) == 0
+    rows_max = (1 << 31) // (64 * 2)                  # bf16, D = 64
+    assert swa.swa_prefill_workspace_bytes(1, rows_max - 200, 1, 64, swa.SWA_BF16) > 0
+    assert swa.swa_prefill_workspace_bytes(1, rows_max, 1, 64, swa.SWA_BF16) == 0
+    assert swa.swa_decode_cache_bytes(1, 1, rows_max - 200, 64) > 0
+    assert swa.swa_decode_cache_bytes(1, 1, rows_max, 64) == 0
+
+
 def test_prefill_argument_checks():
     need = swa.swa_prefill_workspace_bytes(4, 10, 2, 64, swa.SWA_BF16)
     assert need > 0 and need % 256 == 0
