@@ -321,10 +321,12 @@ struct TileLanes {
 };
 
 // Scores: S^T = K Q^T (MFMA; the accumulator of lane l, register i holds
-// key 8*(i/4) + 4*(l/32) + i%4 of each 32-key half and query l%32).
-template <int D, int QB>
+// key 8*(i/4) + 4*(l/32) + i%4 of each 32-key half and query l%32).  The
+// first k-step starts from zero (ZERO) or from init[qb], which the offset
+// softmax uses to subtract each query's offset inside the product.
+template <int D, int QB, bool ZERO>
 __device__ __forceinline__ void tile_scores(const uint16_t* ks, const bf16x8 (&qf)[QB][D / 16], f32x16 (&s)[2][QB],
-                                            const TileLanes<D>& tl) {
+                                            const TileLanes<D>& tl, const f32x16 (&init)[QB]) {
     constexpr int KS = D / 16;
     const f32x16 zero16 = {};
 #pragma unroll
@@ -334,25 +336,20 @@ __device__ __forceinline__ void tile_scores(const uint16_t* ks, const bf16x8 (&q
             const u32x4 a = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(ks + kb * 32 * D) + tl.k[ks_]);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
-                s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[qb][ks_],
-                                                                    ks_ == 0 ? zero16 : s[kb][qb], 0, 0, 0);
+                s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, a), qf[qb][ks_], ks_ == 0 ? (ZERO ? zero16 : init[qb]) : s[kb][qb], 0,
+                    0, 0);
         }
     }
 }
 
-// Online softmax (vector ALUs): keys outside the tile's segment get -inf;
-// new running max m (log2 domain), O and l rescaled when any lane's max
-// moved; P = 2^(s*scale - m) rounded to bf16 into the B operand of the PV
-// product, and l accumulates exactly those bf16 values.
-template <int D, int QB>
-__device__ __forceinline__ void tile_softmax(f32x16 (&s)[2][QB], const Cursor& cur, bf16x8 (&pb)[2][QB][2],
-                                             f32x16 (&o)[QB][D / 32], float (&m)[QB], float (&l)[QB], float sl2,
-                                             int hl) {
-    constexpr int DB = D / 32;
-    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+// Keys outside the tile's segment get score -inf (rare path: tiles at
+// segment edges).
+template <int QB>
+__device__ __forceinline__ void tile_mask(f32x16 (&s)[2][QB], const Cursor& cur, int hl) {
     if (cur.base < cur.lo || cur.base + KT > cur.hi) {
-        // rare path: its 32 per-lane key offsets must not be hoisted into
-        // registers held across the whole loop
+        // its 32 per-lane key offsets must not be hoisted into registers
+        // held across the whole loop
         int hx = hl;
         asm volatile("" : "+v"(hx));
 #pragma unroll
@@ -366,6 +363,19 @@ __device__ __forceinline__ void tile_softmax(f32x16 (&s)[2][QB], const Cursor& c
                 }
             }
     }
+}
+
+// Online softmax (vector ALUs): keys outside the tile's segment get -inf;
+// new running max m (log2 domain), O and l rescaled when any lane's max
+// moved; P = 2^(s*scale - m) rounded to bf16 into the B operand of the PV
+// product, and l accumulates exactly those bf16 values.
+template <int D, int QB>
+__device__ __forceinline__ void tile_softmax(f32x16 (&s)[2][QB], const Cursor& cur, bf16x8 (&pb)[2][QB][2],
+                                             f32x16 (&o)[QB][D / 32], float (&m)[QB], float (&l)[QB], float sl2,
+                                             int hl) {
+    constexpr int DB = D / 32;
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    tile_mask<QB>(s, cur, hl);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         float mx = s[0][qb][0];
@@ -424,17 +434,98 @@ __device__ __forceinline__ void tile_pv(const uint16_t* vs, const bf16x8 (&pb)[2
             }
 }
 
-// One tile of the straightforward schedule, all three phases in order.
+// Offset softmax.  Softmax is unchanged by a per-query shift of the scores,
+// so instead of a running maximum each query keeps one offset m for the
+// whole key range: the maximum of its scores in the range's first tile.
+// Q is pre-scaled by log2(e)/sqrt(D) (rounded to bf16), and the score
+// product of every later tile starts from -m, so it yields s - m directly:
+// per tile only P = 2^(s - m) (rounded to bf16 for the PV product), and the
+// row sum l over those bf16 values remain on the vector ALUs.  Later scores
+// may exceed m; P > 1 is fine while it stays far from overflow, which the
+// caller checks on l at the end (l is at least 1 and below 2^64 unless the
+// scores of the range spread by more than about 40 in log2 units) and
+// otherwise recomputes the range with the running-max softmax.
 template <int D, int QB>
-__device__ __forceinline__ void basic_tile(const uint16_t* ks, const uint16_t* vs, const Cursor& cur,
-                                           const bf16x8 (&qf)[QB][D / 16], f32x16 (&o)[QB][D / 32], float (&m)[QB],
-                                           float (&l)[QB], float sl2, int l32, int hl) {
+struct Acc {
+    bf16x8 qf[QB][D / 16];   // Q^T operands
+    f32x16 o[QB][D / 32];    // O^T accumulators
+    float m[QB], l[QB];      // running max or offset (log2 domain) and row sum, per lane
+    f32x16 c0[QB];           // offset softmax: score accumulator start, -m of the lane's query
+};
+
+enum TileMode { kOnline = 0, kFirst = 1, kOffset = 2 };
+
+// P = 2^s as bf16 into the B operand of the PV product; l accumulates
+// exactly those bf16 values (v_dot2 against ones).
+template <int QB>
+__device__ __forceinline__ void tile_exp(const f32x16 (&s)[2][QB], bf16x8 (&pb)[2][QB][2], float (&l)[QB]) {
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        float ls = l[qb];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p0 = __builtin_amdgcn_exp2f(s[kb][qb][hf * 8 + 2 * e]);
+                    const float p1 = __builtin_amdgcn_exp2f(s[kb][qb][hf * 8 + 2 * e + 1]);
+                    w[e] = pack_bf2(p0, p1);
+                    ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, ls, false);
+                }
+                pb[kb][qb][hf] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+            }
+        l[qb] = ls;
+    }
+}
+
+// First tile of the offset softmax: m = the query's maximum score of the
+// tile (the tile holds at least one key of the range), scores shifted by
+// it, and the accumulator start block -m for the later tiles.
+template <int QB>
+__device__ __forceinline__ void tile_first_offset(f32x16 (&s)[2][QB], float (&m)[QB], f32x16 (&c0)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        float mx = s[0][qb][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][qb][i]);
+        mx = xhalf_max(mx);
+        m[qb] = mx;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb][qb][i] -= mx;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c0[qb][i] = -mx;
+    }
+}
+
+// One 64-key tile for one wave: scores, softmax (running max, or offset),
+// PV product.
+template <int D, int QB, int MODE>
+__device__ __forceinline__ void tile_step(const uint16_t* ks, const uint16_t* vs, const Cursor& cur, Acc<D, QB>& a,
+                                          float sl2, int l32, int hl) {
     f32x16 s[2][QB];
     bf16x8 pb[2][QB][2];
     const TileLanes<D> tl(l32, hl);
-    tile_scores<D, QB>(ks, qf, s, tl);
-    tile_softmax<D, QB>(s, cur, pb, o, m, l, sl2, hl);
-    tile_pv<D, QB>(vs, pb, o, tl);
+    if constexpr (MODE == kOnline) {
+        tile_scores<D, QB, true>(ks, a.qf, s, tl, a.c0);
+        tile_softmax<D, QB>(s, cur, pb, a.o, a.m, a.l, sl2, hl);
+    } else if constexpr (MODE == kFirst) {
+        tile_scores<D, QB, true>(ks, a.qf, s, tl, a.c0);
+        tile_mask<QB>(s, cur, hl);
+        tile_first_offset<QB>(s, a.m, a.c0);
+        tile_exp<QB>(s, pb, a.l);
+    } else {
+        tile_scores<D, QB, false>(ks, a.qf, s, tl, a.c0);
+        tile_mask<QB>(s, cur, hl);
+        tile_exp<QB>(s, pb, a.l);
+    }
+    tile_pv<D, QB>(vs, pb, a.o, tl);
 }
 
 // Work-group barrier after this wave's LDS accesses and all but its N
@@ -457,12 +548,11 @@ __device__ __forceinline__ void sync_tiles() {
 // it + NB - 1, then compute.  U is a compile-time constant and every buffer
 // is an LDS variable of its own, so the compiler can tell the buffer being
 // read from the ones being loaded (with one array it waited for all loads).
-template <int D, int NW, int QB, int NB, int U, class Src>
+template <int D, int NW, int QB, int NB, int U, int MODE, class Src>
 __device__ __forceinline__ void ring_iter(int it, int ntiles, Cursor (&cq)[NB], Cursor& ld, const Src& segs,
                                           const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
-                                          uint16_t* const (&kbuf)[kMaxBufs], uint16_t* const (&vbuf)[kMaxBufs], const bf16x8 (&qf)[QB][D / 16],
-                                          f32x16 (&o)[QB][D / 32], float (&m)[QB], float (&l)[QB], float sl2,
-                                          int tid) {
+                                          uint16_t* const (&kbuf)[kMaxBufs], uint16_t* const (&vbuf)[kMaxBufs],
+                                          Acc<D, QB>& a, float sl2, int tid) {
     using TO = TileOffsets<D, NW>;
     constexpr int PER_TILE = TO::NK + TO::NV;    // load instructions per wave per tile
     constexpr int NXT = (U + NB - 1) % NB;
@@ -484,33 +574,30 @@ __device__ __forceinline__ void ring_iter(int it, int ntiles, Cursor (&cq)[NB], 
         cq[NXT] = ld;
         tile_load<D, NW>(off, kh, vh, ld.base, kbuf[NXT], vbuf[NXT], wave);
     }
-    basic_tile<D, QB>(kcur, vcur, cur, qf, o, m, l, sl2, lane & 31, lane >> 5);
+    tile_step<D, QB, MODE>(kcur, vcur, cur, a, sl2, lane & 31, lane >> 5);
 }
 
-template <int D, int NW, int QB, int NB, int U, class Src>
+template <int D, int NW, int QB, int NB, int U, int MODE, class Src>
 __device__ __forceinline__ void ring_tail(int it, int ntiles, Cursor (&cq)[NB], Cursor& ld, const Src& segs,
                                           const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
-                                          uint16_t* const (&kbuf)[kMaxBufs], uint16_t* const (&vbuf)[kMaxBufs], const bf16x8 (&qf)[QB][D / 16],
-                                          f32x16 (&o)[QB][D / 32], float (&m)[QB], float (&l)[QB], float sl2,
-                                          int tid) {
+                                          uint16_t* const (&kbuf)[kMaxBufs], uint16_t* const (&vbuf)[kMaxBufs],
+                                          Acc<D, QB>& a, float sl2, int tid) {
     if constexpr (U < NB) {
         if (it < ntiles) {
-            ring_iter<D, NW, QB, NB, U>(it, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, qf, o, m, l, sl2, tid);
-            ring_tail<D, NW, QB, NB, U + 1>(it + 1, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, qf, o, m, l, sl2,
-                                            tid);
+            ring_iter<D, NW, QB, NB, U, MODE>(it, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, a, sl2, tid);
+            ring_tail<D, NW, QB, NB, U + 1, MODE>(it + 1, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, a, sl2, tid);
         }
     }
 }
 
-template <int D, int NW, int QB, int NB, int U, class Src>
+template <int D, int NW, int QB, int NB, int U, int MODE, class Src>
 __device__ __forceinline__ void ring_round(int it, int ntiles, Cursor (&cq)[NB], Cursor& ld, const Src& segs,
                                            const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
-                                           uint16_t* const (&kbuf)[kMaxBufs], uint16_t* const (&vbuf)[kMaxBufs], const bf16x8 (&qf)[QB][D / 16],
-                                           f32x16 (&o)[QB][D / 32], float (&m)[QB], float (&l)[QB], float sl2,
-                                           int tid) {
+                                           uint16_t* const (&kbuf)[kMaxBufs], uint16_t* const (&vbuf)[kMaxBufs],
+                                           Acc<D, QB>& a, float sl2, int tid) {
     if constexpr (U < NB) {
-        ring_iter<D, NW, QB, NB, U>(it + U, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, qf, o, m, l, sl2, tid);
-        ring_round<D, NW, QB, NB, U + 1>(it, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, qf, o, m, l, sl2, tid);
+        ring_iter<D, NW, QB, NB, U, MODE>(it + U, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, a, sl2, tid);
+        ring_round<D, NW, QB, NB, U + 1, MODE>(it, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, a, sl2, tid);
     }
 }
 
@@ -528,18 +615,102 @@ __device__ __forceinline__ void decode_token_write(const AttnParams& p, int h, i
     }
 }
 
-// One work item: query tile `qt` of (frame, head h) against key tiles
-// [t_begin, t_end) of the segment list, finished by write_out(piece).
-template <int D, int NW, int QB, bool PREFILL, bool IND = false>
-__device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<PREFILL, IND>& segs, int h, int frame,
-                                             int qt, int t_begin, int t_end, int piece, uint16_t* const (&KB)[kMaxBufs],
-                                             uint16_t* const (&VB)[kMaxBufs], int tid) {
-    using Sh = Shape<NW, QB>;
+// Q^T operands of this wave's query blocks (rows past the frame: zero),
+// multiplied by `scale` and rounded to bf16 when scale != 0.
+template <int D, int QB>
+__device__ __forceinline__ void load_q(const AttnParams& p, int frame, int h, int qrow0, int l32, int hl, float scale,
+                                       bf16x8 (&qf)[QB][D / 16]) {
     constexpr int KS = D / 16;
-    constexpr int DB = D / 32;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int r = qrow0 + qb * 32 + l32;
+        const bool ok = r < p.nq;
+        const int64_t g = (static_cast<int64_t>(frame) * p.nq + (ok ? r : 0)) * p.rs + h * p.hs;
+        const uint16_t* src = static_cast<const uint16_t*>(p.q) + g + hl * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 u = ok ? *reinterpret_cast<const u32x4*>(src + ks * 16) : u32x4{0u, 0u, 0u, 0u};
+            if (scale != 0.f) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    u[j] = pack_bf2(__builtin_bit_cast(float, u[j] << 16) * scale,
+                                    __builtin_bit_cast(float, u[j] & 0xffff0000u) * scale);
+            }
+            qf[qb][ks] = __builtin_bit_cast(bf16x8, u);
+        }
+    }
+}
+
+// One pass over key tiles [t_begin, t_begin + ntiles) of the segment list
+// (ntiles >= 1): the running-max softmax (OFFSET = false) or the offset
+// softmax (OFFSET = true, Q pre-scaled).
+template <int D, int NW, int QB, bool OFFSET, class Src>
+__device__ __forceinline__ void run_pass(const AttnParams& p, const Src& segs, int frame, int h, int qrow0,
+                                         int t_begin, int ntiles, const TileOffsets<D, NW>& off, const uint16_t* kh,
+                                         const uint16_t* vh, uint16_t* const (&KB)[kMaxBufs],
+                                         uint16_t* const (&VB)[kMaxBufs], Acc<D, QB>& a, int tid) {
     constexpr int NB = kRing;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS destinations stay scalar
+    const int l32 = lane & 31;
+    const int hl = lane >> 5;
+
+    // prologue: tiles 0 .. NB-2 in flight
+    Cursor cq[NB];
+    Cursor ld = cursor_at(segs, t_begin);
+#pragma unroll
+    for (int u = 0; u < NB - 1; ++u) {
+        if (u > 0) cursor_next(segs, &ld);
+        cq[u] = ld;
+        if (u < ntiles) tile_load<D, NW>(off, kh, vh, ld.base, KB[u], VB[u], wave);
+    }
+
+    load_q<D, QB>(p, frame, h, qrow0, l32, hl, OFFSET ? p.scale_log2 : 0.f, a.qf);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        a.m[qb] = -INFINITY;
+        a.l[qb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) a.o[qb][db][i] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a.c0[qb][i] = 0.f;
+    }
+    const float sl2 = p.scale_log2;
+
+    if constexpr (OFFSET) {
+        ring_iter<D, NW, QB, NB, 0, kFirst>(0, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
+        ring_tail<D, NW, QB, NB, 1, kOffset>(1, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
+        int it = NB;
+        for (; it + NB <= ntiles; it += NB)
+            ring_round<D, NW, QB, NB, 0, kOffset>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
+        ring_tail<D, NW, QB, NB, 0, kOffset>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
+    } else {
+        int it = 0;
+        for (; it + NB <= ntiles; it += NB)
+            ring_round<D, NW, QB, NB, 0, kOnline>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
+        ring_tail<D, NW, QB, NB, 0, kOnline>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
+    }
+}
+
+#ifndef SWA_OFFSET_SOFTMAX
+#define SWA_OFFSET_SOFTMAX 1
+#endif
+
+// One work item: query tile `qt` of (frame, head h) against key tiles
+// [t_begin, t_end) of the segment list, finished by write_out(piece).  The
+// offset-softmax pass runs first; if any of the work-group's queries ends
+// with a row sum that is not finite or not below 2^64 (its scores spread
+// too far for one fixed offset), the whole work-group recomputes the item
+// with the running-max softmax.  badw: one LDS flag per wave.
+template <int D, int NW, int QB, bool PREFILL, bool IND = false>
+__device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<PREFILL, IND>& segs, int h, int frame,
+                                             int qt, int t_begin, int t_end, int piece, uint16_t* const (&KB)[kMaxBufs],
+                                             uint16_t* const (&VB)[kMaxBufs], int* badw, int tid) {
+    using Sh = Shape<NW, QB>;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;
     const int hl = lane >> 5;
     const int ntiles = t_end - t_begin;
@@ -558,51 +729,24 @@ __device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<P
         }
     }
 
-    // prologue: tiles 0 .. NB-2 in flight
-    Cursor cq[NB];
-    Cursor ld = cursor_at(segs, t_begin);
-#pragma unroll
-    for (int u = 0; u < NB - 1; ++u) {
-        if (u > 0) cursor_next(segs, &ld);
-        cq[u] = ld;
-        if (u < ntiles) tile_load<D, NW>(off, kh, vh, ld.base, KB[u], VB[u], wave);
-    }
-
-    // Q^T operands
     const int qrow0 = qt * Sh::QROWS + wave * QB * 32;
-    bf16x8 qf[QB][KS];
+    Acc<D, QB> a;
+    bool online = !SWA_OFFSET_SOFTMAX;
+    if constexpr (SWA_OFFSET_SOFTMAX) {
+        run_pass<D, NW, QB, true>(p, segs, frame, h, qrow0, t_begin, ntiles, off, kh, vh, KB, VB, a, tid);
+        bool bad = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int r = qrow0 + qb * 32 + l32;
-        const bool ok = r < p.nq;
-        const int64_t g = (static_cast<int64_t>(frame) * p.nq + (ok ? r : 0)) * p.rs + h * p.hs;
-        const uint16_t* src = static_cast<const uint16_t*>(p.q) + g + hl * 8;
+        for (int qb = 0; qb < QB; ++qb) bad = bad || !(a.l[qb] < 0x1p64f);
+        const bool wbad = __builtin_amdgcn_ballot_w64(bad) != 0;
+        if (lane == 0) badw[wave] = wbad ? 1 : 0;
+        sync_tiles<0>();                             // every wave's flag, and every wave done with the tiles
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 u = ok ? *reinterpret_cast<const u32x4*>(src + ks * 16) : u32x4{0u, 0u, 0u, 0u};
-            qf[qb][ks] = __builtin_bit_cast(bf16x8, u);
-        }
+        for (int w = 0; w < NW; ++w) online = online || badw[w] != 0;
     }
+    if (online)
+        run_pass<D, NW, QB, false>(p, segs, frame, h, qrow0, t_begin, ntiles, off, kh, vh, KB, VB, a, tid);
 
-    f32x16 o[QB][DB];
-    float m[QB], l[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        m[qb] = -INFINITY;
-        l[qb] = 0.f;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[qb][db][i] = 0.f;
-    }
-    const float sl2 = p.scale_log2;
-
-    int it = 0;
-    for (; it + NB <= ntiles; it += NB)
-        ring_round<D, NW, QB, NB, 0>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, qf, o, m, l, sl2, tid);
-    ring_tail<D, NW, QB, NB, 0>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, qf, o, m, l, sl2, tid);
-
-    write_out<D, QB, PREFILL>(p, o, m, l, qrow0, frame, h, piece, l32, hl);
+    write_out<D, QB, PREFILL>(p, a.o, a.m, a.l, qrow0, frame, h, piece, l32, hl);
 }
 
 // Work decomposition.  Prefill: one work item per (frame, head, query tile).
@@ -632,6 +776,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t V2[NB > 2 ? D * KT : 8];
     __shared__ __attribute__((aligned(16))) uint16_t V3[NB > 3 ? D * KT : 8];
     __shared__ __attribute__((aligned(16))) uint16_t V4[NB > 4 ? D * KT : 8];
+    __shared__ int badw[NW];
     uint16_t* const KB[kMaxBufs] = {K0, K1, K2, K3, K4};
     uint16_t* const VB[kMaxBufs] = {V0, V1, V2, V3, V4};
 
@@ -643,7 +788,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnParams p) {
         const int h = item % p.H;
         const int frame = p.F - 1 - item / p.H;          // heaviest frames first
         const SegSrc<true> segs{p, prefill_segs(frame, p.W, p.S, p.fP)};
-        attend_range<D, NW, QB, true>(p, segs, h, frame, qt, 0, segs.total(), -1, KB, VB, tid);
+        attend_range<D, NW, QB, true>(p, segs, h, frame, qt, 0, segs.total(), -1, KB, VB, badw, tid);
     } else {
         const SegSrc<false, IND> segs{p, PreSegs{}};
         const int n = segs.total();
@@ -660,7 +805,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnParams p) {
             const int t1 = static_cast<int>(f1 - h0 < n ? f1 - h0 : n);
             const int piece = (t0 == 0 && t1 == n) ? -1 : 2 * item + (first ? 0 : 1);
             if (!first) sync_tiles<0>();                 // every wave is done with the last range's tiles
-            attend_range<D, NW, QB, false, IND>(p, segs, h, 0, qt, t0, t1, piece, KB, VB, tid);
+            attend_range<D, NW, QB, false, IND>(p, segs, h, 0, qt, t0, t1, piece, KB, VB, badw, tid);
             f = h0 + t1;
             first = false;
         }
