@@ -461,33 +461,48 @@ class NaiveRingCache:
         return out, lse, pages
 
 
-def stream_replay(cfg: CacheConfig, frames, keyframe_of=lambda t: True, steps=None,
-                  pos_of=None, rope_pairs=None, theta=10000.0, record=None):
-    """Feed frames one per step through a NaiveRingCache.
+def stream_replay(cfg: CacheConfig, frames, steps: int, keyframe_of=lambda t: True, pos_of=None,
+                  rope_pairs=None, theta: float = 10000.0, record=None, rows=None, store=None):
+    """Feed frames 0 .. steps-1 through one layer's NaiveRingCache, one per step.
 
-    frames(t) -> (q, k, v) for frame t.  With pos_of/rope_pairs given, q and
-    k are rotated before the append (RoPE is applied before caching in the
-    block's pre-attention step).  Returns a list of per-step dicts for the
-    steps listed in `record` (all if None): out, lse, pages.
+    A generator.  frames(t) -> (q, k, v), each [P, H, D], for frame t.  Each
+    step follows the streaming branch of FlashInferBlock.forward: a keyframe
+    appends, evicts and attends; a non-keyframe (keyframe_of(t) false)
+    appends with eviction deferred, attends and rolls back.  With pos_of(t)
+    -> int [P, 3] and rope_pairs = (pairs_t, pairs_h, pairs_w), k is rotated
+    by rope3d before it enters the cache and q before it attends (the
+    block's pre-attention step rotates both before caching and attention).
+    store, if given, is applied to the rotated q and k: it models the
+    precision of the tensors that hold them (the rotation itself stays
+    exact).
+
+    Yields (t, pages, out, lse) per step: the visible-page records the step
+    attended over and, for steps in `record` (every step if None), the
+    attention output [n, H, D] and LSE [H, n] of query rows `rows` (all P
+    rows if None); otherwise out and lse are None.
     """
     cache = NaiveRingCache(cfg)
-    results = {}
-    n = steps if steps is not None else 0
-    for t in range(n):
+    for t in range(steps):
         q, k, v = frames(t)
-        if pos_of is not None:
-            pos = pos_of(t)
-            q = rope3d(q, pos, *rope_pairs, theta=theta)
+        keyframe = bool(keyframe_of(t))
+        pos = pos_of(t) if pos_of is not None else None
+        if pos is not None:
             k = rope3d(k, pos, *rope_pairs, theta=theta)
-        kf = keyframe_of(t)
+            if store is not None:
+                k = store(k)
+        cache.append(t, k, v, keyframe)
+        if keyframe:
+            cache.evict()
+        pages = cache.visible_pages()
+        out = lse = None
         if record is None or t in record:
-            out, lse, pages = cache.step(t, q, k, v, kf)
-            results[t] = {"out": out, "lse": lse, "pages": pages}
-        else:
-            # state still advances exactly as in a recorded step
-            cache.append(t, k, v, kf)
-            if kf:
-                cache.evict()
-            else:
-                cache.rollback()
-    return results, cache
+            sel = slice(None) if rows is None else rows
+            qs = q[sel]
+            if pos is not None:
+                qs = rope3d(qs, pos[sel], *rope_pairs, theta=theta)
+                if store is not None:
+                    qs = store(qs)
+            out, lse = cache.attend(qs)
+        if not keyframe:
+            cache.rollback()
+        yield t, pages, out, lse

@@ -455,10 +455,13 @@ struct Acc {
 
 enum TileMode { kOnline = 0, kFirst = 1, kOffset = 2 };
 
-// P = 2^s as bf16 into the B operand of the PV product; l accumulates
-// exactly those bf16 values (v_dot2 against ones).
-template <int QB>
-__device__ __forceinline__ void tile_exp(const f32x16 (&s)[2][QB], bf16x8 (&pb)[2][QB][2], float (&l)[QB]) {
+// P = 2^x as bf16 into the B operand of the PV product, with x = s (the
+// offset already inside the score product) or x = s * sl2 - m (FMA, Q not
+// pre-scaled); l accumulates exactly those bf16 values (v_dot2 against
+// ones).
+template <int QB, bool FMA>
+__device__ __forceinline__ void tile_exp(const f32x16 (&s)[2][QB], bf16x8 (&pb)[2][QB][2], float (&l)[QB],
+                                         const float (&m)[QB], float sl2) {
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -470,8 +473,9 @@ __device__ __forceinline__ void tile_exp(const f32x16 (&s)[2][QB], bf16x8 (&pb)[
                 uint32_t w[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float p0 = __builtin_amdgcn_exp2f(s[kb][qb][hf * 8 + 2 * e]);
-                    const float p1 = __builtin_amdgcn_exp2f(s[kb][qb][hf * 8 + 2 * e + 1]);
+                    const float x0 = s[kb][qb][hf * 8 + 2 * e], x1 = s[kb][qb][hf * 8 + 2 * e + 1];
+                    const float p0 = __builtin_amdgcn_exp2f(FMA ? fmaf(x0, sl2, -m[qb]) : x0);
+                    const float p1 = __builtin_amdgcn_exp2f(FMA ? fmaf(x1, sl2, -m[qb]) : x1);
                     w[e] = pack_bf2(p0, p1);
                     ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, ls, false);
                 }
@@ -481,11 +485,12 @@ __device__ __forceinline__ void tile_exp(const f32x16 (&s)[2][QB], bf16x8 (&pb)[
     }
 }
 
-// First tile of the offset softmax: m = the query's maximum score of the
-// tile (the tile holds at least one key of the range), scores shifted by
-// it, and the accumulator start block -m for the later tiles.
-template <int QB>
-__device__ __forceinline__ void tile_first_offset(f32x16 (&s)[2][QB], float (&m)[QB], f32x16 (&c0)[QB]) {
+// First tile of the offset softmax: m = the query's maximum scaled score
+// of the tile (the tile holds at least one key of the range).  Pre-scaled
+// Q (PRE): the scores are shifted by m here and the accumulator start block
+// -m serves the later tiles; otherwise each tile's exponent is one FMA.
+template <int QB, bool PRE>
+__device__ __forceinline__ void tile_first_offset(f32x16 (&s)[2][QB], float (&m)[QB], f32x16 (&c0)[QB], float sl2) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         float mx = s[0][qb][0];
@@ -494,15 +499,24 @@ __device__ __forceinline__ void tile_first_offset(f32x16 (&s)[2][QB], float (&m)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][qb][i]);
         mx = xhalf_max(mx);
-        m[qb] = mx;
+        if constexpr (PRE) {
+            m[qb] = mx;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[kb][qb][i] -= mx;
+                for (int i = 0; i < 16; ++i) s[kb][qb][i] -= mx;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) c0[qb][i] = -mx;
+            for (int i = 0; i < 16; ++i) c0[qb][i] = -mx;
+        } else {
+            m[qb] = mx * sl2;
+        }
     }
 }
+
+#ifndef SWA_PRESCALE_Q
+#define SWA_PRESCALE_Q 0
+#endif
+constexpr bool kPrescaleQ = SWA_PRESCALE_Q != 0;
 
 // One 64-key tile for one wave: scores, softmax (running max, or offset),
 // PV product.
@@ -518,12 +532,12 @@ __device__ __forceinline__ void tile_step(const uint16_t* ks, const uint16_t* vs
     } else if constexpr (MODE == kFirst) {
         tile_scores<D, QB, true>(ks, a.qf, s, tl, a.c0);
         tile_mask<QB>(s, cur, hl);
-        tile_first_offset<QB>(s, a.m, a.c0);
-        tile_exp<QB>(s, pb, a.l);
+        tile_first_offset<QB, kPrescaleQ>(s, a.m, a.c0, sl2);
+        tile_exp<QB, !kPrescaleQ>(s, pb, a.l, a.m, sl2);
     } else {
-        tile_scores<D, QB, false>(ks, a.qf, s, tl, a.c0);
+        tile_scores<D, QB, !kPrescaleQ>(ks, a.qf, s, tl, a.c0);
         tile_mask<QB>(s, cur, hl);
-        tile_exp<QB>(s, pb, a.l);
+        tile_exp<QB, !kPrescaleQ>(s, pb, a.l, a.m, sl2);
     }
     tile_pv<D, QB>(vs, pb, a.o, tl);
 }
@@ -665,7 +679,7 @@ __device__ __forceinline__ void run_pass(const AttnParams& p, const Src& segs, i
         if (u < ntiles) tile_load<D, NW>(off, kh, vh, ld.base, KB[u], VB[u], wave);
     }
 
-    load_q<D, QB>(p, frame, h, qrow0, l32, hl, OFFSET ? p.scale_log2 : 0.f, a.qf);
+    load_q<D, QB>(p, frame, h, qrow0, l32, hl, OFFSET && kPrescaleQ ? p.scale_log2 : 0.f, a.qf);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         a.m[qb] = -INFINITY;

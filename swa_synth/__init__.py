@@ -35,11 +35,20 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
-    """bfloat16 bit patterns (uint16) of float32 values, round to nearest even."""
+    """bfloat16 bit patterns (uint16) of float32 values, round to nearest even.
+
+    Adding 0x7FFF plus the kept part's lowest bit and dropping the low 16
+    bits rounds to nearest, ties to even.  In 32-bit unsigned arithmetic this
+    wraps only for NaN patterns, which are replaced by the quiet NaN after.
+    """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    r = u >> 16
+    r &= 1
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= 16
+    r = r.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         r[nan] = 0x7FC0

@@ -42,3 +42,29 @@ def bf16_round_f64(x):
     """float64 -> nearest bfloat16 value (via torch's RNE conversion on CPU)."""
     return torch.from_numpy(np.asarray(x, np.float64)).to(torch.float32).to(torch.bfloat16).to(
         torch.float64).numpy()
+
+
+def lse_tol(n_keys):
+    """Tolerance on the fp32 LSE of one query row over n_keys visible keys.
+
+    Per key, the kernel rounds each probability to bf16 (relative error up
+    to 2^-9, independent across keys): about 1.1e-3 RMS, so the LSE moves by
+    about 1.1e-3 * sqrt(sum_j a_j^2) with a_j the softmax weights.  For
+    N(0,1) inputs (scaled scores ~ N(0, 1)) sum_j a_j^2 averages e / n over
+    rows, with a wide spread when n is small (one key can dominate), so that
+    term is bounded by 0.01 * sqrt(min(1, 8 / n)) (about six standard
+    deviations).  Per query, the row sum is accumulated in fp32 over up to
+    tens of thousands of terms and a rotated or normalised q is held in
+    bf16; measured at full size these add up to about 2e-4, covered by a
+    floor of 3e-4.  A lost or doubled 64-key tile moves the LSE by about
+    64 / n (1.9e-3 at 32,976 keys), above the bound at every size; the q = 0
+    closed-form tests check the key count exactly (LSE = ln n to 1e-5).
+    """
+    return 0.01 * float(np.sqrt(min(1.0, 8.0 / n_keys))) + 3e-4
+
+
+def ulp_bf16(x):
+    """Spacing of bfloat16 values at |x| (normal range)."""
+    a = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return 2.0 ** (e - 7)

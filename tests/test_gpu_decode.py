@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import sliding_window_kv_amd as swa
-from gpu_helpers import assert_close_bf16, case, dev, host
+from gpu_helpers import assert_close_bf16, case, dev, host, lse_tol
 from oracle import RollingDecodeCache
 from swa_synth import frame_qkv
 
@@ -42,7 +42,7 @@ def test_decode_matches_oracle(B, Hq, Hkv, W, D):
             oc[b].append(pos, k[b], v[b])
             ro[b], rl[b] = oc[b].attend(pos, q[b])
         assert_close_bf16(host(out), ro, f"pos={pos}")
-        assert np.abs(host(lse) - rl).max() <= 1e-2, f"lse pos={pos}"
+        assert np.abs(host(lse) - rl).max() <= lse_tol(min(pos + 1, W)), f"lse pos={pos}"
     # the buffers hold exactly the last W tokens' bf16 keys and values
     rows = (W + 64 + 63) // 64 * 64
     raw = dc.cache.view(torch.bfloat16).float().cpu().numpy()
@@ -72,4 +72,4 @@ def test_decode_full_window_sampled():
         if pos in check:
             ro, rl = oc.attend(pos, q[0])
             assert_close_bf16(host(out)[0], ro, f"pos={pos}")
-            assert np.abs(host(lse)[0] - rl).max() <= 1e-2
+            assert np.abs(host(lse)[0] - rl).max() <= lse_tol(min(pos + 1, W))

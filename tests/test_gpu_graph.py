@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import sliding_window_kv_amd as swa
-from gpu_helpers import assert_close_bf16, bf16_round_f64, case, dev, host
+from gpu_helpers import assert_close_bf16, bf16_round_f64, case, dev, host, lse_tol
 from oracle import CacheConfig, NaiveRingCache, head_layer_norm, rope3d
 from swa_synth import frame_positions, frame_qkv, norm_weights
 
@@ -83,11 +83,11 @@ def _run(P, H, D, W, S, L, T, keyframe_of=lambda t: True, cross=False, ns=5, R=1
             if norm or any(rope):
                 qn, kn = bf16_round_f64(qn), bf16_round_f64(kn)
             if oracle_at is None or t in oracle_at:
-                ro, rl, _ = _oracle_step(ocs[l], t, qn, kn, v, kf, rows)
+                ro, rl, pages = _oracle_step(ocs[l], t, qn, kn, v, kf, rows)
                 got = host(outs[l]) if rows is None else host(outs[l])[rows]
                 gl = host(lses[l]) if rows is None else host(lses[l])[:, rows]
                 assert_close_bf16(got, ro, f"oracle layer {l} t={t}")
-                assert np.abs(gl - rl).max() <= 1e-2, f"lse layer {l} t={t}"
+                assert np.abs(gl - rl).max() <= lse_tol(sum(p[4] for p in pages)), f"lse layer {l} t={t}"
                 # after the step (a non-keyframe is rolled back again)
                 assert gcache.pages(l) == [tuple(p) for p in ocs[l].visible_pages()], f"pages layer {l} t={t}"
             else:
