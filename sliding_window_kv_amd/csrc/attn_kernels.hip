@@ -33,6 +33,8 @@
 //    segment get score -inf and their V^T elements are cleared in LDS.
 #include <math.h>
 
+#include <algorithm>
+
 #include "launch.hpp"
 
 namespace swa {
@@ -513,14 +515,11 @@ __device__ __forceinline__ void tile_first_offset(f32x16 (&s)[2][QB], float (&m)
     }
 }
 
-#ifndef SWA_PRESCALE_Q
-#define SWA_PRESCALE_Q 0
-#endif
-constexpr bool kPrescaleQ = SWA_PRESCALE_Q != 0;
 
 // One 64-key tile for one wave: scores, softmax (running max, or offset),
-// PV product.
-template <int D, int QB, int MODE>
+// PV product.  PRE: the offset softmax with Q pre-scaled (offset inside the
+// score product); otherwise Q exact and the exponent one FMA.
+template <int D, int QB, int MODE, bool PRE>
 __device__ __forceinline__ void tile_step(const uint16_t* ks, const uint16_t* vs, const Cursor& cur, Acc<D, QB>& a,
                                           float sl2, int l32, int hl) {
     f32x16 s[2][QB];
@@ -532,12 +531,12 @@ __device__ __forceinline__ void tile_step(const uint16_t* ks, const uint16_t* vs
     } else if constexpr (MODE == kFirst) {
         tile_scores<D, QB, true>(ks, a.qf, s, tl, a.c0);
         tile_mask<QB>(s, cur, hl);
-        tile_first_offset<QB, kPrescaleQ>(s, a.m, a.c0, sl2);
-        tile_exp<QB, !kPrescaleQ>(s, pb, a.l, a.m, sl2);
+        tile_first_offset<QB, PRE>(s, a.m, a.c0, sl2);
+        tile_exp<QB, !PRE>(s, pb, a.l, a.m, sl2);
     } else {
-        tile_scores<D, QB, !kPrescaleQ>(ks, a.qf, s, tl, a.c0);
+        tile_scores<D, QB, !PRE>(ks, a.qf, s, tl, a.c0);
         tile_mask<QB>(s, cur, hl);
-        tile_exp<QB, !kPrescaleQ>(s, pb, a.l, a.m, sl2);
+        tile_exp<QB, !PRE>(s, pb, a.l, a.m, sl2);
     }
     tile_pv<D, QB>(vs, pb, a.o, tl);
 }
@@ -562,7 +561,7 @@ __device__ __forceinline__ void sync_tiles() {
 // it + NB - 1, then compute.  U is a compile-time constant and every buffer
 // is an LDS variable of its own, so the compiler can tell the buffer being
 // read from the ones being loaded (with one array it waited for all loads).
-template <int D, int NW, int QB, int NB, int U, int MODE, class Src>
+template <int D, int NW, int QB, int NB, int U, int MODE, bool PRE, class Src>
 __device__ __forceinline__ void ring_iter(int it, int ntiles, Cursor (&cq)[NB], Cursor& ld, const Src& segs,
                                           const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
                                           uint16_t* const (&kbuf)[kMaxBufs], uint16_t* const (&vbuf)[kMaxBufs],
@@ -588,30 +587,30 @@ __device__ __forceinline__ void ring_iter(int it, int ntiles, Cursor (&cq)[NB], 
         cq[NXT] = ld;
         tile_load<D, NW>(off, kh, vh, ld.base, kbuf[NXT], vbuf[NXT], wave);
     }
-    tile_step<D, QB, MODE>(kcur, vcur, cur, a, sl2, lane & 31, lane >> 5);
+    tile_step<D, QB, MODE, PRE>(kcur, vcur, cur, a, sl2, lane & 31, lane >> 5);
 }
 
-template <int D, int NW, int QB, int NB, int U, int MODE, class Src>
+template <int D, int NW, int QB, int NB, int U, int MODE, bool PRE, class Src>
 __device__ __forceinline__ void ring_tail(int it, int ntiles, Cursor (&cq)[NB], Cursor& ld, const Src& segs,
                                           const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
                                           uint16_t* const (&kbuf)[kMaxBufs], uint16_t* const (&vbuf)[kMaxBufs],
                                           Acc<D, QB>& a, float sl2, int tid) {
     if constexpr (U < NB) {
         if (it < ntiles) {
-            ring_iter<D, NW, QB, NB, U, MODE>(it, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, a, sl2, tid);
-            ring_tail<D, NW, QB, NB, U + 1, MODE>(it + 1, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, a, sl2, tid);
+            ring_iter<D, NW, QB, NB, U, MODE, PRE>(it, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, a, sl2, tid);
+            ring_tail<D, NW, QB, NB, U + 1, MODE, PRE>(it + 1, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, a, sl2, tid);
         }
     }
 }
 
-template <int D, int NW, int QB, int NB, int U, int MODE, class Src>
+template <int D, int NW, int QB, int NB, int U, int MODE, bool PRE, class Src>
 __device__ __forceinline__ void ring_round(int it, int ntiles, Cursor (&cq)[NB], Cursor& ld, const Src& segs,
                                            const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
                                            uint16_t* const (&kbuf)[kMaxBufs], uint16_t* const (&vbuf)[kMaxBufs],
                                            Acc<D, QB>& a, float sl2, int tid) {
     if constexpr (U < NB) {
-        ring_iter<D, NW, QB, NB, U, MODE>(it + U, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, a, sl2, tid);
-        ring_round<D, NW, QB, NB, U + 1, MODE>(it, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, a, sl2, tid);
+        ring_iter<D, NW, QB, NB, U, MODE, PRE>(it + U, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, a, sl2, tid);
+        ring_round<D, NW, QB, NB, U + 1, MODE, PRE>(it, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, a, sl2, tid);
     }
 }
 
@@ -657,8 +656,8 @@ __device__ __forceinline__ void load_q(const AttnParams& p, int frame, int h, in
 
 // One pass over key tiles [t_begin, t_begin + ntiles) of the segment list
 // (ntiles >= 1): the running-max softmax (OFFSET = false) or the offset
-// softmax (OFFSET = true, Q pre-scaled).
-template <int D, int NW, int QB, bool OFFSET, class Src>
+// softmax (OFFSET = true; PRE: with Q pre-scaled).
+template <int D, int NW, int QB, bool OFFSET, bool PRE, class Src>
 __device__ __forceinline__ void run_pass(const AttnParams& p, const Src& segs, int frame, int h, int qrow0,
                                          int t_begin, int ntiles, const TileOffsets<D, NW>& off, const uint16_t* kh,
                                          const uint16_t* vh, uint16_t* const (&KB)[kMaxBufs],
@@ -679,7 +678,7 @@ __device__ __forceinline__ void run_pass(const AttnParams& p, const Src& segs, i
         if (u < ntiles) tile_load<D, NW>(off, kh, vh, ld.base, KB[u], VB[u], wave);
     }
 
-    load_q<D, QB>(p, frame, h, qrow0, l32, hl, OFFSET && kPrescaleQ ? p.scale_log2 : 0.f, a.qf);
+    load_q<D, QB>(p, frame, h, qrow0, l32, hl, OFFSET && PRE ? p.scale_log2 : 0.f, a.qf);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         a.m[qb] = -INFINITY;
@@ -694,31 +693,28 @@ __device__ __forceinline__ void run_pass(const AttnParams& p, const Src& segs, i
     const float sl2 = p.scale_log2;
 
     if constexpr (OFFSET) {
-        ring_iter<D, NW, QB, NB, 0, kFirst>(0, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
-        ring_tail<D, NW, QB, NB, 1, kOffset>(1, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
+        ring_iter<D, NW, QB, NB, 0, kFirst, PRE>(0, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
+        ring_tail<D, NW, QB, NB, 1, kOffset, PRE>(1, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
         int it = NB;
         for (; it + NB <= ntiles; it += NB)
-            ring_round<D, NW, QB, NB, 0, kOffset>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
-        ring_tail<D, NW, QB, NB, 0, kOffset>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
+            ring_round<D, NW, QB, NB, 0, kOffset, PRE>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
+        ring_tail<D, NW, QB, NB, 0, kOffset, PRE>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
     } else {
         int it = 0;
         for (; it + NB <= ntiles; it += NB)
-            ring_round<D, NW, QB, NB, 0, kOnline>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
-        ring_tail<D, NW, QB, NB, 0, kOnline>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
+            ring_round<D, NW, QB, NB, 0, kOnline, false>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
+        ring_tail<D, NW, QB, NB, 0, kOnline, false>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
     }
 }
 
-#ifndef SWA_OFFSET_SOFTMAX
-#define SWA_OFFSET_SOFTMAX 1
-#endif
-
 // One work item: query tile `qt` of (frame, head h) against key tiles
 // [t_begin, t_end) of the segment list, finished by write_out(piece).  The
-// offset-softmax pass runs first; if any of the work-group's queries ends
-// with a row sum that is not finite or not below 2^64 (its scores spread
-// too far for one fixed offset), the whole work-group recomputes the item
-// with the running-max softmax.  badw: one LDS flag per wave.
-template <int D, int NW, int QB, bool PREFILL, bool IND = false>
+// offset-softmax pass runs first (PRE: with Q pre-scaled); if any of the
+// work-group's queries ends with a row sum that is not finite or not below
+// 2^64 (its scores spread too far for one fixed offset), the whole
+// work-group recomputes the item with the running-max softmax.  badw: one
+// LDS flag per wave.
+template <int D, int NW, int QB, bool PREFILL, bool IND, bool PRE>
 __device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<PREFILL, IND>& segs, int h, int frame,
                                              int qt, int t_begin, int t_end, int piece, uint16_t* const (&KB)[kMaxBufs],
                                              uint16_t* const (&VB)[kMaxBufs], int* badw, int tid) {
@@ -733,10 +729,11 @@ __device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<P
     const uint16_t* vh = static_cast<const uint16_t*>(p.vreg) + static_cast<size_t>(h) * D * p.rows;
     const TileOffsets<D, NW> off(p.rows, wave, lane);
 
-    if constexpr (!PREFILL) {
-        // token decode: the one work item whose range holds the new slot's
-        // tile (the buffer's single segment starts at row 0) writes the new
-        // token first; its stores complete before the tile loads below
+    if constexpr (!PREFILL && NW == 1) {
+        // token decode (one-wave work-groups): the one work item whose range
+        // holds the new slot's tile (the buffer's single segment starts at
+        // row 0) writes the new token first; its stores complete before the
+        // tile loads below
         if (p.dk != nullptr && p.dslot / KT >= t_begin && p.dslot / KT < t_end) {
             decode_token_write<D, NW>(p, h, tid);
             sync_tiles<0>();
@@ -745,20 +742,18 @@ __device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<P
 
     const int qrow0 = qt * Sh::QROWS + wave * QB * 32;
     Acc<D, QB> a;
-    bool online = !SWA_OFFSET_SOFTMAX;
-    if constexpr (SWA_OFFSET_SOFTMAX) {
-        run_pass<D, NW, QB, true>(p, segs, frame, h, qrow0, t_begin, ntiles, off, kh, vh, KB, VB, a, tid);
-        bool bad = false;
+    run_pass<D, NW, QB, true, PRE>(p, segs, frame, h, qrow0, t_begin, ntiles, off, kh, vh, KB, VB, a, tid);
+    bool bad = false;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) bad = bad || !(a.l[qb] < 0x1p64f);
-        const bool wbad = __builtin_amdgcn_ballot_w64(bad) != 0;
-        if (lane == 0) badw[wave] = wbad ? 1 : 0;
-        sync_tiles<0>();                             // every wave's flag, and every wave done with the tiles
+    for (int qb = 0; qb < QB; ++qb) bad = bad || !(a.l[qb] < 0x1p64f);
+    const bool wbad = __builtin_amdgcn_ballot_w64(bad) != 0;
+    if (lane == 0) badw[wave] = wbad ? 1 : 0;
+    sync_tiles<0>();                                 // every wave's flag, and every wave done with the tiles
+    bool online = false;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) online = online || badw[w] != 0;
-    }
+    for (int w = 0; w < NW; ++w) online = online || badw[w] != 0;
     if (online)
-        run_pass<D, NW, QB, false>(p, segs, frame, h, qrow0, t_begin, ntiles, off, kh, vh, KB, VB, a, tid);
+        run_pass<D, NW, QB, false, false>(p, segs, frame, h, qrow0, t_begin, ntiles, off, kh, vh, KB, VB, a, tid);
 
     write_out<D, QB, PREFILL>(p, a.o, a.m, a.l, qrow0, frame, h, piece, l32, hl);
 }
@@ -774,8 +769,11 @@ __device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<P
 // (work-groups the GPU holds) / qtiles, every work-group gets the same
 // number of tiles and the launch finishes in one round.  IND (captured
 // steps): the segments come from device memory and the launch has a fixed
-// number of columns, of which the first min(ncols, H * n) work.
-template <int D, int NW, int QB, int OCC, bool PREFILL, bool IND = false>
+// number of columns, of which the first min(ncols, H * n) work.  PRE: the
+// offset softmax with Q pre-scaled, chosen when no LSE is requested (its
+// bf16 rounding of the scaled Q shifts a query's LSE by up to about 2^-9 of
+// its score magnitude, but leaves the output within bf16 noise).
+template <int D, int NW, int QB, int OCC, bool PREFILL, bool IND, bool PRE>
 __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnParams p) {
     constexpr int NB = kRing;
     static_assert(NB >= 2 && NB <= kMaxBufs, "2 to 5 tile buffers");
@@ -802,7 +800,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnParams p) {
         const int h = item % p.H;
         const int frame = p.F - 1 - item / p.H;          // heaviest frames first
         const SegSrc<true> segs{p, prefill_segs(frame, p.W, p.S, p.fP)};
-        attend_range<D, NW, QB, true>(p, segs, h, frame, qt, 0, segs.total(), -1, KB, VB, badw, tid);
+        attend_range<D, NW, QB, true, false, PRE>(p, segs, h, frame, qt, 0, segs.total(), -1, KB, VB, badw, tid);
     } else {
         const SegSrc<false, IND> segs{p, PreSegs{}};
         const int n = segs.total();
@@ -819,7 +817,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnParams p) {
             const int t1 = static_cast<int>(f1 - h0 < n ? f1 - h0 : n);
             const int piece = (t0 == 0 && t1 == n) ? -1 : 2 * item + (first ? 0 : 1);
             if (!first) sync_tiles<0>();                 // every wave is done with the last range's tiles
-            attend_range<D, NW, QB, false, IND>(p, segs, h, 0, qt, t0, t1, piece, KB, VB, badw, tid);
+            attend_range<D, NW, QB, false, IND, PRE>(p, segs, h, 0, qt, t0, t1, piece, KB, VB, badw, tid);
             f = h0 + t1;
             first = false;
         }
@@ -1049,14 +1047,25 @@ constexpr int kNW = SWA_NW;       // waves per work-group
 constexpr int kQB = SWA_QB;       // 32-query blocks per wave
 constexpr int kOcc = SWA_OCC;     // waves per SIMD the register budget targets
 
+template <int D, bool PRE>
+void attn_bf16_launch(bool prefill, const AttnParams& p, int grid, hipStream_t stream) {
+    if (!prefill && p.dseg != nullptr)
+        hipLaunchKernelGGL((attn_bf16_kernel<D, kNW, kQB, kOcc, false, true, PRE>), dim3(grid), dim3(kNW * 64), 0,
+                           stream, p);
+    else if (prefill)
+        hipLaunchKernelGGL((attn_bf16_kernel<D, kNW, kQB, kOcc, true, false, PRE>), dim3(grid), dim3(kNW * 64), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((attn_bf16_kernel<D, kNW, kQB, kOcc, false, false, PRE>), dim3(grid), dim3(kNW * 64), 0,
+                           stream, p);
+}
+
 template <int D>
 hipError_t attn_bf16_dispatch(bool prefill, const AttnParams& p, int grid, hipStream_t stream) {
-    if (!prefill && p.dseg != nullptr)
-        hipLaunchKernelGGL((attn_bf16_kernel<D, kNW, kQB, kOcc, false, true>), dim3(grid), dim3(kNW * 64), 0, stream, p);
-    else if (prefill)
-        hipLaunchKernelGGL((attn_bf16_kernel<D, kNW, kQB, kOcc, true>), dim3(grid), dim3(kNW * 64), 0, stream, p);
+    if (p.lse == nullptr)
+        attn_bf16_launch<D, true>(prefill, p, grid, stream);
     else
-        hipLaunchKernelGGL((attn_bf16_kernel<D, kNW, kQB, kOcc, false>), dim3(grid), dim3(kNW * 64), 0, stream, p);
+        attn_bf16_launch<D, false>(prefill, p, grid, stream);
     return hipGetLastError();
 }
 
@@ -1072,13 +1081,22 @@ hipError_t attn_f32_dispatch(bool prefill, const AttnParams& p, hipStream_t stre
 
 }  // namespace
 
+template <typename K>
+int blocks_per_cu_of(K kernel, int threads) {
+    int n = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0);
+    return (e == hipSuccess && n > 0) ? n : 1;
+}
+
+// The fewer of the two softmax variants' resident work-groups (the
+// automatic split sizes one launch round with it).
 int attention_blocks_per_cu(int dtype, int D) {
     if (dtype != 0) return 1;
-    int n = 0;
-    const hipError_t e =
-        D == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, kNW, kQB, kOcc, false>, kNW * 64, 0)
-                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<32, kNW, kQB, kOcc, false>, kNW * 64, 0);
-    return (e == hipSuccess && n > 0) ? n : 1;
+    if (D == 64)
+        return std::min(blocks_per_cu_of(attn_bf16_kernel<64, kNW, kQB, kOcc, false, false, false>, kNW * 64),
+                        blocks_per_cu_of(attn_bf16_kernel<64, kNW, kQB, kOcc, false, false, true>, kNW * 64));
+    return std::min(blocks_per_cu_of(attn_bf16_kernel<32, kNW, kQB, kOcc, false, false, false>, kNW * 64),
+                    blocks_per_cu_of(attn_bf16_kernel<32, kNW, kQB, kOcc, false, false, true>, kNW * 64));
 }
 
 int attention_q_tile(int dtype) { return dtype == 0 ? Shape<kNW, kQB>::QROWS : 64; }
@@ -1088,18 +1106,23 @@ int attention_q_tile(int dtype) { return dtype == 0 ? Shape<kNW, kQB>::QROWS : 6
 int attention_decode_q_rows() { return Shape<1, 1>::QROWS; }
 
 int attention_decode_blocks_per_cu(int D) {
-    int n = 0;
-    const hipError_t e =
-        D == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, 1, 1, kOcc, false>, 64, 0)
-                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<32, 1, 1, kOcc, false>, 64, 0);
-    return (e == hipSuccess && n > 0) ? n : 1;
+    return D == 64 ? blocks_per_cu_of(attn_bf16_kernel<64, 1, 1, kOcc, false, false, false>, 64)
+                   : blocks_per_cu_of(attn_bf16_kernel<32, 1, 1, kOcc, false, false, false>, 64);
 }
 
+template <int D, bool PRE>
+void decode_launch(const AttnParams& p, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_bf16_kernel<D, 1, 1, kOcc, false, false, PRE>), dim3(grid), dim3(64), 0, stream, p);
+}
+
+// Decode keeps Q exact: it is bound by HBM, not by the softmax's vector
+// work, and the pre-scaled variant would need more registers than two waves
+// per SIMD allow.
 hipError_t launch_attention_decode(int D, const AttnParams& p, int grid, hipStream_t stream) {
     if (D == 64)
-        hipLaunchKernelGGL((attn_bf16_kernel<64, 1, 1, kOcc, false>), dim3(grid), dim3(64), 0, stream, p);
+        decode_launch<64, false>(p, grid, stream);
     else
-        hipLaunchKernelGGL((attn_bf16_kernel<32, 1, 1, kOcc, false>), dim3(grid), dim3(64), 0, stream, p);
+        decode_launch<32, false>(p, grid, stream);
     return hipGetLastError();
 }
 
