@@ -366,6 +366,24 @@ int swa_decode_step(void* cache, size_t cache_bytes, int B, int Hq, int Hkv, int
                     size_t work_bytes, swa_stream_t stream);
 
 /*
+ * For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid allocation): swa_decode_step
+ * with its split partials in a static device array of
+ * SWA_DECODE_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds on each
+ * GPU it runs on until the process ends, instead of a caller workspace.  Same
+ * arguments, kernels, work split and results as swa_decode_step.  Allocates
+ * nothing; the first call on a device looks up the array's device address.
+ * Limit: (Hq / Hkv) * (head_dim + 2) <= 1024 (15 query heads per kv head at
+ * head_dim 64, 30 at 32), else SWA_E_CAPACITY.  Every call on one GPU shares
+ * its array: calls that overlap on one GPU (different streams, or threads)
+ * race and must be serialised by the caller.
+ */
+#define SWA_DECODE_NOALLOC_SCRATCH_BYTES (16u << 20)
+int swa_decode_step_noalloc(void* cache, size_t cache_bytes, int B, int Hq, int Hkv, int W, int D, int64_t pos,
+                            const void* q, const void* k, const void* v, void* out, float* lse,
+                            swa_stream_t stream);
+
+/*
  * Masked prefill of F frames submitted at once ([G] "Mask Generation in
  * CausalAttention"): query frame i sees key frame j iff j <= i and
  * (j >= i - W + 1 or j < scale_frames), W = sliding_window_size *

@@ -83,6 +83,7 @@ _PROTOS = {
     "swa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "swa_decode_step": (_i32, [_vp, _sz, _i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                _vp]),
+    "swa_decode_step_noalloc": (_i32, [_vp, _sz, _i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "swa_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "swa_prefill_masked": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                   _vp, _sz, _vp]),
@@ -215,6 +216,10 @@ def swa_decode_step(cache, cache_bytes, B, Hq, Hkv, W, D, pos, q, k, v, out, lse
                                        stream))
 
 
+def swa_decode_step_noalloc(cache, cache_bytes, B, Hq, Hkv, W, D, pos, q, k, v, out, lse, stream=None):
+    return check(lib().swa_decode_step_noalloc(cache, cache_bytes, B, Hq, Hkv, W, D, pos, q, k, v, out, lse, stream))
+
+
 class DecodeCache:
     """Rolling buffers of B sequences for token decode (device memory from torch)."""
 
@@ -235,6 +240,11 @@ class DecodeCache:
     def step(self, pos, q, k, v, out, lse=None):
         swa_decode_step(_ptr(self.cache), self.nbytes, self.B, self.Hq, self.Hkv, self.W, self.D, pos, _ptr(q),
                         _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(self.work), self.wbytes, _stream())
+
+    def step_noalloc(self, pos, q, k, v, out, lse=None):
+        """The same step with the split partials in the library's static scratch (no workspace)."""
+        swa_decode_step_noalloc(_ptr(self.cache), self.nbytes, self.B, self.Hq, self.Hkv, self.W, self.D, pos,
+                                _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _stream())
 
 
 def swa_prefill_workspace_bytes(F, P, H, D, dtype):

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libswa.so")
 
-SOURCES = ["attn_kernels.hip", "kv_kernels.hip", "ring.cpp", "swa_api.cpp"]
+SOURCES = ["attn_kernels.hip", "kv_kernels.hip", "ring.cpp", "swa_api.cpp", "decode_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.

@@ -10,6 +10,7 @@
 #include <type_traits>
 #include <vector>
 
+#include "api_internal.hpp"
 #include "launch.hpp"
 #include "ring.hpp"
 #include "swa.h"
@@ -554,7 +555,7 @@ int rope3d_apply(void* q, void* k, const int32_t* pos, int n_tokens, int H, int 
 
 namespace {
 
-constexpr int kMaxDecodeCols = 2048;         // columns of one decode call (2 partial slots each)
+using swa::kMaxDecodeCols;
 
 struct DecodeLayout {
     int64_t rows, k_bytes, total;            // K and V^T regions of the rolling buffers
@@ -568,10 +569,7 @@ DecodeLayout decode_layout(int B, int Hkv, int W, int D) {
     return d;
 }
 
-int64_t decode_work_bytes(int G, int D) {
-    const int64_t pieces = 2 * int64_t(kMaxDecodeCols);
-    return align_up(pieces * G * D * 4, 256) + align_up(pieces * G * 2 * 4, 256);
-}
+int64_t decode_work_bytes(int G, int D) { return swa::decode_partials_bytes(G, D, kMaxDecodeCols); }
 
 // Resident decode work-groups on the current device (cached per device).
 int decode_fit(int D) {
@@ -660,67 +658,13 @@ size_t swa_decode_workspace_bytes(int Hq, int Hkv, int D) {
 int swa_decode_step(void* cache, size_t cache_bytes, int B, int Hq, int Hkv, int W, int D, int64_t pos,
                     const void* q, const void* k, const void* v, void* out, float* lse, void* work,
                     size_t work_bytes, swa_stream_t stream) {
-    if (cache == nullptr || q == nullptr || k == nullptr || v == nullptr || out == nullptr || work == nullptr)
-        return fail(SWA_E_INVAL, "null pointer");
-    if (B < 1 || Hkv < 1 || Hq < 1 || W < 1) return fail(SWA_E_INVAL, "B, Hq, Hkv and W must be >= 1");
-    if (D != 32 && D != 64) return fail(SWA_E_UNSUPPORTED, "head_dim must be 32 or 64");
-    if (Hq % Hkv != 0) return fail(SWA_E_INVAL, "Hq must be a multiple of Hkv");
-    const int G = Hq / Hkv;
-    if (G > swa::attention_decode_q_rows()) return fail(SWA_E_UNSUPPORTED, "more than 32 query heads per kv head");
-    if (pos < 0) return fail(SWA_E_INVAL, "position must be >= 0");
-    if (int64_t(W) + 128 > (1ll << 30) || !row_space_fits(W, D, 2)) return fail(SWA_E_INVAL, "window too large");
-    const DecodeLayout dl = decode_layout(B, Hkv, W, D);
-    if (cache_bytes < static_cast<size_t>(dl.total)) return fail(SWA_E_INVAL, "cache smaller than swa_decode_cache_bytes()");
-    if (work_bytes < static_cast<size_t>(decode_work_bytes(G, D)))
+    if (work == nullptr) return fail(SWA_E_INVAL, "null pointer");
+    if (Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0 && (D == 32 || D == 64) &&
+        work_bytes < static_cast<size_t>(decode_work_bytes(Hq / Hkv, D)))
         return fail(SWA_E_INVAL, "workspace smaller than swa_decode_workspace_bytes()");
-    if (reinterpret_cast<uintptr_t>(cache) % 256 != 0 || reinterpret_cast<uintptr_t>(work) % 256 != 0)
-        return fail(SWA_E_INVAL, "cache and workspace must be 256-byte aligned");
-    const int nh = B * Hkv;
-    void* kreg = cache;
-    void* vreg = static_cast<char*>(cache) + dl.k_bytes;
-    const int slot = static_cast<int>(pos % W);
-
-    const int n = static_cast<int>(std::min<int64_t>(pos + 1, W));   // live slots 0..n-1
-    swa::AttnParams p{};
-    p.q = q;
-    p.kreg = kreg;
-    p.vreg = vreg;
-    p.out = out;
-    p.lse = lse;
-    p.nq = G;
-    p.H = nh;
-    p.rs = D;
-    p.hs = int64_t(G) * D;
-    p.rows = static_cast<int>(dl.rows);
-    p.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
-    p.F = 1;
-    p.seg.n = 1;
-    for (int i = 0; i < swa::kMaxSegs; ++i) {
-        p.seg.lo[i] = p.seg.hi[i] = 0;
-        p.seg.tile0[i] = 1 << 30;
-    }
-    p.seg.lo[0] = 0;
-    p.seg.hi[0] = n;
-    p.seg.tile0[0] = 0;
-    const int tiles = tiles_of(0, n);
-    p.seg.total_tiles = tiles;
-    p.qtiles = 1;
-    int64_t cols = std::min<int64_t>(decode_fit(D), kMaxDecodeCols);
-    cols = std::max<int64_t>(1, std::min<int64_t>(cols, int64_t(nh) * tiles));
-    p.ncols = static_cast<int>(cols);
-    const int64_t pieces = 2 * int64_t(kMaxDecodeCols);
-    p.dk = k;                                   // the new token goes in with the attention launch
-    p.dv = v;
-    p.dslot = slot;
-    p.part_o = static_cast<float*>(work);
-    p.part_ml = reinterpret_cast<float*>(static_cast<char*>(work) + align_up(pieces * G * D * 4, 256));
-    hipError_t e = swa::launch_attention_decode(D, p, p.ncols, stream);
-    if (e != hipSuccess) return hip_fail(e, "decode attention kernel launch");
-    if (!(p.ncols <= nh && nh % p.ncols == 0)) {
-        e = swa::launch_merge(D, nh, G, tiles, p.ncols, p.part_o, p.part_ml, out, lse, p.rs, p.hs, nullptr, stream);
-        if (e != hipSuccess) return hip_fail(e, "decode merge kernel launch");
-    }
-    return SWA_OK;
+    if (reinterpret_cast<uintptr_t>(work) % 256 != 0) return fail(SWA_E_INVAL, "workspace must be 256-byte aligned");
+    return swa::decode_step_impl(cache, cache_bytes, B, Hq, Hkv, W, D, pos, q, k, v, out, lse, work, kMaxDecodeCols,
+                                 stream);
 }
 
 size_t swa_prefill_workspace_bytes(int F, int P, int H, int D, int dtype) {
@@ -911,3 +855,79 @@ int swa_graph_destroy(swa_graph* g) {
 const char* swa_last_error(void) { return g_err.c_str(); }
 
 }  // extern "C"
+
+namespace swa {
+
+int api_fail(int code, const char* msg) { return fail(code, msg); }
+
+int64_t decode_partials_bytes(int G, int D, int max_cols) {
+    const int64_t pieces = 2 * int64_t(max_cols);
+    return align_up(pieces * G * D * 4, 256) + align_up(pieces * G * 2 * 4, 256);
+}
+
+int decode_step_impl(void* cache, size_t cache_bytes, int B, int Hq, int Hkv, int W, int D, int64_t pos,
+                     const void* q, const void* k, const void* v, void* out, float* lse, void* part, int max_cols,
+                     hipStream_t stream) {
+    if (cache == nullptr || q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+        return fail(SWA_E_INVAL, "null pointer");
+    if (B < 1 || Hkv < 1 || Hq < 1 || W < 1) return fail(SWA_E_INVAL, "B, Hq, Hkv and W must be >= 1");
+    if (D != 32 && D != 64) return fail(SWA_E_UNSUPPORTED, "head_dim must be 32 or 64");
+    if (Hq % Hkv != 0) return fail(SWA_E_INVAL, "Hq must be a multiple of Hkv");
+    const int G = Hq / Hkv;
+    if (G > attention_decode_q_rows()) return fail(SWA_E_UNSUPPORTED, "more than 32 query heads per kv head");
+    if (pos < 0) return fail(SWA_E_INVAL, "position must be >= 0");
+    if (int64_t(W) + 128 > (1ll << 30) || !row_space_fits(W, D, 2)) return fail(SWA_E_INVAL, "window too large");
+    if (part == nullptr || max_cols < 1) return fail(SWA_E_INVAL, "no split-partial space");
+    const DecodeLayout dl = decode_layout(B, Hkv, W, D);
+    if (cache_bytes < static_cast<size_t>(dl.total)) return fail(SWA_E_INVAL, "cache smaller than swa_decode_cache_bytes()");
+    if (reinterpret_cast<uintptr_t>(cache) % 256 != 0) return fail(SWA_E_INVAL, "cache must be 256-byte aligned");
+    if (int64_t(B) * Hkv > (1 << 24)) return fail(SWA_E_INVAL, "too many sequences x kv heads");
+    const int nh = B * Hkv;
+    void* kreg = cache;
+    void* vreg = static_cast<char*>(cache) + dl.k_bytes;
+    const int slot = static_cast<int>(pos % W);
+
+    const int n = static_cast<int>(std::min<int64_t>(pos + 1, W));   // live slots 0..n-1
+    AttnParams p{};
+    p.q = q;
+    p.kreg = kreg;
+    p.vreg = vreg;
+    p.out = out;
+    p.lse = lse;
+    p.nq = G;
+    p.H = nh;
+    p.rs = D;
+    p.hs = int64_t(G) * D;
+    p.rows = static_cast<int>(dl.rows);
+    p.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
+    p.F = 1;
+    p.seg.n = 1;
+    for (int i = 0; i < kMaxSegs; ++i) {
+        p.seg.lo[i] = p.seg.hi[i] = 0;
+        p.seg.tile0[i] = 1 << 30;
+    }
+    p.seg.lo[0] = 0;
+    p.seg.hi[0] = n;
+    p.seg.tile0[0] = 0;
+    const int tiles = tiles_of(0, n);
+    p.seg.total_tiles = tiles;
+    p.qtiles = 1;
+    int64_t cols = std::min<int64_t>(decode_fit(D), max_cols);
+    cols = std::max<int64_t>(1, std::min<int64_t>(cols, int64_t(nh) * tiles));
+    p.ncols = static_cast<int>(cols);
+    const int64_t pieces = 2 * int64_t(max_cols);
+    p.dk = k;                                   // the new token goes in with the attention launch
+    p.dv = v;
+    p.dslot = slot;
+    p.part_o = static_cast<float*>(part);
+    p.part_ml = reinterpret_cast<float*>(static_cast<char*>(part) + align_up(pieces * G * D * 4, 256));
+    hipError_t e = launch_attention_decode(D, p, p.ncols, stream);
+    if (e != hipSuccess) return hip_fail(e, "decode attention kernel launch");
+    if (!(p.ncols <= nh && nh % p.ncols == 0)) {
+        e = launch_merge(D, nh, G, tiles, p.ncols, p.part_o, p.part_ml, out, lse, p.rs, p.hs, nullptr, stream);
+        if (e != hipSuccess) return hip_fail(e, "decode merge kernel launch");
+    }
+    return SWA_OK;
+}
+
+}  // namespace swa

@@ -197,6 +197,20 @@ def test_decode_argument_checks():
     assert e.value.code == swa.SWA_E_INVAL
 
 
+def test_decode_noalloc_argument_checks():
+    # the allocation-free decode rejects argument errors and group sizes whose
+    # split partials exceed its 16 MiB static scratch before touching the GPU
+    p = ctypes.c_void_p(256)
+    need = swa.swa_decode_cache_bytes(1, 4, 64, 64)
+    for args, code in [((p, need, 1, 64, 4, 64, 64, 0), swa.SWA_E_CAPACITY),     # 16 query heads per kv head, D 64
+                       ((p, need, 1, 62, 2, 64, 32, 0), swa.SWA_E_CAPACITY),     # 31 per kv head, D 32
+                       ((p, need, 1, 6, 4, 64, 64, 0), swa.SWA_E_INVAL),         # Hq not a multiple of Hkv
+                       ((p, need, 1, 8, 4, 64, 48, 0), swa.SWA_E_UNSUPPORTED)]:  # head_dim 48
+        with pytest.raises(swa.SwaError) as e:
+            swa.swa_decode_step_noalloc(*args, p, p, p, p, None)
+        assert e.value.code == code
+
+
 def _pair(P, W, S, cross, ns, R, max_frames=50):
     ocfg = CacheConfig(P=P, sliding_window_size=W, scale_frames=S, cross_frame_special=cross,
                        special_row0=0, special_rows=ns, max_special_frames=R, max_frames=max_frames)
