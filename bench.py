@@ -147,18 +147,21 @@ def _cpu(value, unit, sample):
     return {"value": round(value, 6), "unit": unit, "cores": _cores(), "kind": "oracle", "sample": sample}
 
 
-# The attention kernel's sources and the build script that holds its compile
-# flags: a traffic summary under profiles/ applies while their hash matches.
+# The attention kernel's sources and its compile flags: a traffic summary
+# under profiles/ applies while their hash matches.
 KERNEL_SOURCES = ("sliding_window_kv_amd/csrc/attn_kernels.hip", "sliding_window_kv_amd/csrc/kernels_common.hpp",
-                  "sliding_window_kv_amd/build.py")
+                  "sliding_window_kv_amd/csrc/launch.hpp")
 
 
 def _sources_sha256(paths):
     import hashlib
+    from sliding_window_kv_amd import build as B
     h = hashlib.sha256()
     for rel in paths:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    flags = B.COMMON + B.DEVICE_FLAGS + B.PER_SOURCE_FLAGS.get("attn_kernels.hip", [])
+    h.update(" ".join(x.replace(ROOT, "<repo>") for x in flags).encode())
     return h.hexdigest()
 
 
