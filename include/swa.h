@@ -127,10 +127,12 @@ typedef struct swa_page {
  * Where the cache keeps its rows inside the caller's pool (bytes from the
  * pool base).  Per layer l, with E = element size:
  *   K   at k_offset + l*layer_bytes, laid out [H][rows][D]
- *   V^T at v_offset + l*layer_bytes, laid out [H][D][rows], where key r is
- *       stored at position r with bits 2 and 3 swapped (a permutation inside
- *       every aligned group of 16 keys; it matches the key order of one MFMA
- *       lane's operand).
+ *   V^T at v_offset + l*layer_bytes, laid out [H][rows/64][D][64]: blocks
+ *       of 64 key positions, each a [D][64] matrix (rows is a multiple of
+ *       64), where key r is stored at position r with bits 2 and 3 swapped
+ *       (a permutation inside every aligned group of 16 keys; it matches the
+ *       key order of one MFMA lane's operand).  Element (h, d, position s)
+ *       is at ((h * rows/64 + s/64) * D + d) * 64 + s % 64.
  * Page slot s holds a frame in rows [s*P, (s+1)*P); special-ring entry e
  * holds its rows at special_row_base + e*special_rows.
  * The work area [work_offset, work_offset + work_bytes) holds the partial
@@ -341,9 +343,9 @@ int swa_graph_destroy(swa_graph* graph);
  * attention), query head h reads kv head h / (Hq / Hkv).  bf16 only.
  *
  * cache: device buffer of swa_decode_cache_bytes(B, Hkv, W, D) bytes, 256-byte
- *   aligned, caller-owned: K [B*Hkv][rows][D] then V^T [B*Hkv][D][rows]
- *   (rows = W rounded up plus 64 rows of tile padding; V^T keys at vt_pos
- *   as in swa_layout).  Contents need no initialisation: slot s is read only
+ *   aligned, caller-owned: K [B*Hkv][rows][D] then V^T [B*Hkv][rows/64][D][64]
+ *   (rows = W plus 64 rows of tile padding, rounded up to a multiple of 64;
+ *   V^T blocks and key positions as in swa_layout).  Contents need no initialisation: slot s is read only
  *   after a step has written it.
  * swa_decode_step: all B sequences are at the same position pos (>= 0) and
  *   must have been stepped through positions 0 .. pos-1 before.  Writes

@@ -382,7 +382,9 @@ class SwaCache:
         return kvcache_read_device_pages(self.handle, layer, cap, _stream())
 
     def region_views(self, layer=0):
-        """(K [H, rows, D], V^T [H, D, rows]) tensors viewing the layer's rows."""
+        """(K [H, rows, D], V^T [H, rows / 64, D, 64]) tensors viewing the layer's rows.
+
+        V^T is stored in blocks of 64 key positions (see swa_layout in swa.h)."""
         import torch
         L, c = self.layout, self.cfg
         dt = torch.bfloat16 if c.dtype == SWA_BF16 else torch.float32
@@ -390,7 +392,7 @@ class SwaCache:
         H, D, rows = c.num_heads, c.head_dim, L.rows
         nb = H * rows * D * L.elem_bytes
         k = self.pool_view[base + L.k_offset: base + L.k_offset + nb].view(dt).view(H, rows, D)
-        v = self.pool_view[base + L.v_offset: base + L.v_offset + nb].view(dt).view(H, D, rows)
+        v = self.pool_view[base + L.v_offset: base + L.v_offset + nb].view(dt).view(H, rows // 64, D, 64)
         return k, v
 
 

@@ -13,11 +13,13 @@
 //  * A work-group of NW waves owns NW*QB*32 query rows of one frame and head.
 //    Each wave holds Q^T for QB blocks of 32 queries in registers as the B
 //    operand of v_mfma_f32_32x32x16_bf16.
-//  * Keys stream through LDS in tiles of 64 rows, in a ring of kRing
-//    buffers (kRing - 1 tiles in flight while one is consumed), loaded with
-//    direct global->LDS 16-byte loads (no staging registers).  K is
-//    kept as [64][D], V^T as [D][64]; 16-byte chunks are XOR-swizzled by row
-//    so the MFMA operand reads are free of bank conflicts.
+//  * Keys stream through LDS in 64-aligned tiles of 64 rows, in a ring of
+//    kRing buffers (kRing - 1 tiles in flight while one is consumed), loaded
+//    with direct global->LDS 16-byte loads (no staging registers).  A tile
+//    is a contiguous 64 x D block of K rows and, with V^T stored in blocks of
+//    64 keys, a contiguous [D][64] block of V^T; in LDS both are kept in that
+//    shape with 16-byte chunks XOR-swizzled by row, so the MFMA operand reads
+//    are free of bank conflicts.
 //  * S^T = K Q^T: the accumulator layout puts one query per lane column and
 //    16 keys per lane, so a query's row max needs one cross-half exchange
 //    and the row sum stays lane-local until the end.
@@ -29,7 +31,7 @@
 //    the row sum is taken over the bf16 probabilities the MFMA consumes
 //    (v_dot2), and the O rescale is skipped when no lane's running max
 //    changed.
-//  * Segment edges: tiles start on a 16-row boundary; keys outside the
+//  * Segment edges: tiles start on a 64-row boundary; keys outside the
 //    segment get score -inf and their V^T elements are cleared in LDS.
 #include <math.h>
 
@@ -42,7 +44,7 @@ namespace swa {
 namespace {
 
 constexpr int KT = 64;            // keys per tile
-constexpr int KALIGN = 16;        // tile start alignment (rows)
+constexpr int KALIGN = 64;        // tile start alignment (rows): one V^T block per tile
 #ifndef SWA_RING
 #define SWA_RING 3
 #endif
@@ -247,9 +249,10 @@ __device__ __forceinline__ void write_out(const AttnParams& p, const f32x16 (&o)
 }
 
 // Per-lane element offsets of the 16-byte chunks a thread loads into one
-// K tile ([64][D], swizzled) and one V^T tile ([D][64], swizzled); only the
-// tile's first row changes from tile to tile, so every load is a uniform
-// base plus one of these constant offsets.
+// K tile ([64][D], swizzled) and one V^T tile ([D][64], swizzled) from the
+// tile's K rows and V^T block, each contiguous and starting at element
+// base * D of its head's region: every load is that uniform base plus one
+// of these constant offsets.
 template <int D, int NW>
 struct TileOffsets {
     static constexpr int CPR = D / 8;
@@ -257,7 +260,7 @@ struct TileOffsets {
     static constexpr int NV = D * (KT / 8) / (64 * NW);
     int k[NK];
     int v[NV];
-    __device__ TileOffsets(int rows, int wave, int lane) {
+    __device__ TileOffsets(int wave, int lane) {
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
             const int p = (i * NW + wave) * 64 + lane;
@@ -268,7 +271,7 @@ struct TileOffsets {
         for (int i = 0; i < NV; ++i) {
             const int p = (i * NW + wave) * 64 + lane;
             const int d = p / 8;
-            v[i] = d * rows + ((p % 8) ^ lds_swz<8>(d)) * 8;
+            v[i] = d * KT + ((p % 8) ^ lds_swz<8>(d)) * 8;
         }
     }
 };
@@ -281,7 +284,7 @@ __device__ __forceinline__ void tile_load(const TileOffsets<D, NW>& off, const u
     // scalar base + unsigned 32-bit byte offset: the loads take the
     // SGPR-base form and need no per-load 64-bit address arithmetic
     const char* kt = reinterpret_cast<const char*>(kh + static_cast<size_t>(base) * D);
-    const char* vt = reinterpret_cast<const char*>(vh + base);
+    const char* vt = reinterpret_cast<const char*>(vh + static_cast<size_t>(base) * D);
 #pragma unroll
     for (int i = 0; i < TO::NK; ++i)
         __builtin_amdgcn_global_load_lds(
@@ -621,10 +624,10 @@ __device__ __forceinline__ void decode_token_write(const AttnParams& p, int h, i
     const uint16_t* k = static_cast<const uint16_t*>(p.dk) + static_cast<size_t>(h) * D;
     const uint16_t* v = static_cast<const uint16_t*>(p.dv) + static_cast<size_t>(h) * D;
     uint16_t* kr = static_cast<uint16_t*>(const_cast<void*>(p.kreg)) + (static_cast<size_t>(h) * p.rows + p.dslot) * D;
-    uint16_t* vr = static_cast<uint16_t*>(const_cast<void*>(p.vreg)) + static_cast<size_t>(h) * D * p.rows + vt_pos(p.dslot);
+    uint16_t* vr = static_cast<uint16_t*>(const_cast<void*>(p.vreg)) + static_cast<size_t>(h) * D * p.rows;
     for (int d = tid; d < D; d += NW * 64) {
         kr[d] = k[d];
-        vr[static_cast<size_t>(d) * p.rows] = v[d];
+        vr[vt_elem(d, vt_pos(p.dslot), D)] = v[d];
     }
 }
 
@@ -727,7 +730,7 @@ __device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<P
 
     const uint16_t* kh = static_cast<const uint16_t*>(p.kreg) + static_cast<size_t>(h) * p.rows * D;
     const uint16_t* vh = static_cast<const uint16_t*>(p.vreg) + static_cast<size_t>(h) * D * p.rows;
-    const TileOffsets<D, NW> off(p.rows, wave, lane);
+    const TileOffsets<D, NW> off(wave, lane);
 
     if constexpr (!PREFILL && NW == 1) {
         // token decode (one-wave work-groups): the one work item whose range
@@ -758,7 +761,12 @@ __device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<P
     write_out<D, QB, PREFILL>(p, a.o, a.m, a.l, qrow0, frame, h, piece, l32, hl);
 }
 
-// Work decomposition.  Prefill: one work item per (frame, head, query tile).
+// Work decomposition.  Prefill: one work item per (frame, head, query tile),
+// ordered head-major with the frames of a head from last to first: an XCD
+// (a run of consecutive logical work-groups) then holds neighbouring frames
+// of the same head at once, which share most of their visible key frames
+// (all scale frames and most of the window) through its L2, and within a
+// head the frames that see the most keys start first.
 // Streaming: every query of the frame sees the same key tiles, so the
 // (head, key tile) space of H * n tiles is cut into p.ncols equal columns,
 // and column c runs as p.qtiles work-groups, one per query tile, that walk
@@ -797,8 +805,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnParams p) {
     const int qt = L % p.qtiles;
     const int item = L / p.qtiles;
     if constexpr (PREFILL) {
-        const int h = item % p.H;
-        const int frame = p.F - 1 - item / p.H;          // heaviest frames first
+        const int h = item / p.F;
+        const int frame = p.F - 1 - item % p.F;
         const SegSrc<true> segs{p, prefill_segs(frame, p.W, p.S, p.fP)};
         attend_range<D, NW, QB, true, false, PRE>(p, segs, h, frame, qt, 0, segs.total(), -1, KB, VB, badw, tid);
     } else {
@@ -1021,7 +1029,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
             const float pr = exp2f(s - mnew);
             l = l * alpha + pr;
 #pragma unroll
-            for (int d = 0; d < D; ++d) acc[d] = fmaf(pr, vh[static_cast<size_t>(d) * p.rows + vt_pos(key)], acc[d] * alpha);
+            for (int d = 0; d < D; ++d) acc[d] = fmaf(pr, vh[vt_elem(d, vt_pos(key), D)], acc[d] * alpha);
             m = mnew;
         }
     }

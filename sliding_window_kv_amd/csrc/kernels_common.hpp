@@ -25,6 +25,14 @@ __host__ __device__ __forceinline__ int vt_pos(int key) {
     return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
 }
 
+// Element offset, inside one head's transposed V region, of feature d at
+// storage position s (= vt_pos of the key): the region is a sequence of
+// blocks of 64 positions, each block a [D][64] matrix, so the V^T of a
+// 64-aligned key tile is one contiguous block.
+__host__ __device__ __forceinline__ int vt_elem(int d, int s, int D) {
+    return (s & ~63) * D + d * 64 + (s & 63);
+}
+
 __device__ __forceinline__ float bf2f(uint16_t b) {
     return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
 }

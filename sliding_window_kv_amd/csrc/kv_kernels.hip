@@ -4,10 +4,11 @@
 //
 // Cache layout of one layer (rows = the layer's row space):
 //   K   [H][rows][D]  -- a key row is D contiguous elements
-//   V^T [H][D][rows]  -- transposed, keys stored at vt_pos(key) (bits 2 and 3
-//                        swapped inside each 16-key group), so the attention
-//                        kernel reads the 8 keys one MFMA lane needs as one
-//                        16-byte load
+//   V^T [H][rows/64][D][64] -- transposed in blocks of 64 keys, keys stored
+//                        at vt_pos(key) (bits 2 and 3 swapped inside each
+//                        16-key group), so a 64-aligned key tile's V^T is
+//                        one contiguous block and the attention kernel reads
+//                        the 8 keys one MFMA lane needs as one 16-byte load
 // A frame in page slot s owns rows [s*P, (s+1)*P) (guide "KV Cache Eviction
 // Strategy": whole frames enter and leave the cache).
 #include "launch.hpp"
@@ -129,7 +130,7 @@ __device__ __forceinline__ void row_layer_norm(float (&x)[E], const float* w, co
 
 constexpr int kTileRows = 64;
 
-// One block = 64 destination rows (16-aligned) of one head.
+// One block = 64 destination rows (64-aligned: one V^T block) of one head.
 template <typename T, int D, bool ROPE, bool NORM>
 __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                      T* __restrict__ kreg, T* __restrict__ vreg,
@@ -156,15 +157,15 @@ __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, co
     __shared__ T vt[kTileRows * LD];
 
     const int h = blockIdx.y;
-    const int base = (row0 & ~15) + blockIdx.x * kTileRows;  // first destination row
+    const int base = (row0 & ~63) + blockIdx.x * kTileRows;  // first destination row
     const int tid = threadIdx.x;
 
     if (meta_slot != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *meta_slot = frame_id;
 
     // Retention of the previous occupant's special rows: the block whose
     // rows hold some of them copies those (K rows, and their V^T columns,
-    // which vt_pos keeps inside the same 16-row group) to the special ring,
-    // and only then overwrites them.
+    // whose positions vt_pos keeps inside the same 16-row group) to the
+    // special ring, and only then overwrites them.
     {
         const int lo = ret.src_row > base ? ret.src_row : base;
         const int hi = ret.src_row + ret.ns < base + kTileRows ? ret.src_row + ret.ns : base + kTileRows;
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, co
             for (int i = tid; i < nr * D; i += 256) {
                 const int d = i / nr;
                 const int r = lo + i % nr;
-                vh[static_cast<size_t>(d) * rows + vt_pos(r + shift)] = vh[static_cast<size_t>(d) * rows + vt_pos(r)];
+                vh[vt_elem(d, vt_pos(r + shift), D)] = vh[vt_elem(d, vt_pos(r), D)];
             }
             __syncthreads();                 // every old row read before any is overwritten
         }
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, co
             full = full && valid[e];
             out.e[e] = vt[key * LD + d];
         }
-        T* dst = vreg + (static_cast<size_t>(h) * D + d) * rows + base + kc * E;
+        T* dst = vreg + static_cast<size_t>(h) * D * rows + vt_elem(d, base + kc * E, D);
         if (full) {
             *reinterpret_cast<uint4*>(dst) = out.u;
         } else {
@@ -402,9 +403,9 @@ hipError_t append_dispatch(int H, int n_tok, int row0, int rows, const void* k, 
                            void* kreg, void* vreg, void* q, const int32_t* pos, const RopeArgs* rope,
                            const NormArgs* norm, int32_t* meta_slot, int32_t frame_id, const RetainArgs& ret,
                            const StepPlan* plan, hipStream_t stream) {
-    const int first = row0 & ~15;
-    // with a device plan the first row is not known here: enough tiles for any 16-row offset
-    const int tiles = plan != nullptr ? (15 + n_tok + kTileRows - 1) / kTileRows
+    const int first = row0 & ~63;
+    // with a device plan the first row is not known here: enough tiles for any 64-row offset
+    const int tiles = plan != nullptr ? (63 + n_tok + kTileRows - 1) / kTileRows
                                       : (row0 + n_tok - first + kTileRows - 1) / kTileRows;
     dim3 grid(tiles, H);
     RopeArgs r{};

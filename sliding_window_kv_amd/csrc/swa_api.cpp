@@ -42,9 +42,9 @@ struct Layout {
     int64_t part_o_floats;                               // floats of the O partials
 };
 
-// One head's K or V^T region is addressed with 32-bit offsets inside the
-// kernels (feature d of V^T starts d * rows elements in, loads add a byte
-// offset of twice that): keep D * rows * element size below 2^31.
+// Element offsets inside one head's K or V^T region are 32-bit ints in the
+// kernels (and byte offsets twice that): keep D * rows * element size below
+// 2^31.
 bool row_space_fits(int64_t used_rows, int D, int elem) {
     const int64_t rows = (used_rows + 64 + 63) / 64 * 64;
     return rows * D * elem < (int64_t(1) << 31);
@@ -150,8 +150,8 @@ void make_rope(int pt, int ph, int pw, float theta, swa::RopeArgs* r) {
             r->freq[p++] = std::pow(static_cast<double>(theta), -static_cast<double>(kk) / bands[b]);
 }
 
-// Key tiles of a row segment: 64 rows each, the first starting on a 16-row boundary.
-int tiles_of(int lo, int hi) { return (hi - (lo & ~15) + 63) / 64; }
+// Key tiles of a row segment: 64 rows each, the first starting on a 64-row boundary.
+int tiles_of(int lo, int hi) { return (hi - (lo & ~63) + 63) / 64; }
 
 }  // namespace
 

@@ -9,6 +9,18 @@ BF16_MEAN_ABS = 2e-3
 F32_MAX_ABS = 1e-5
 
 
+def vt_keys(vb):
+    """Transposed V read back from a cache region, in key order.
+
+    vb: [N, rows / 64, D, 64], the documented storage of V^T (blocks of 64
+    key positions, each [D][64]; key r at position r with bits 2 and 3
+    swapped).  Returns [N, D, rows] with column r holding key r."""
+    n, nb, d, _ = vb.shape
+    by_pos = vb.transpose(0, 2, 1, 3).reshape(n, d, nb * 64)
+    r = np.arange(nb * 64)
+    return by_pos[:, :, (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1)]
+
+
 def case(msg):
     print(f"[case] {msg}", flush=True)
 

@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import sliding_window_kv_amd as swa
-from gpu_helpers import assert_close_bf16, case, dev, host, lse_tol
+from gpu_helpers import assert_close_bf16, case, dev, host, lse_tol, vt_keys
 from oracle import RollingDecodeCache
 from swa_synth import frame_qkv
 
@@ -17,10 +17,6 @@ def _token(cfg, pos, B, Hq, Hkv, D):
     _, k, v = frame_qkv(cfg, pos, B, Hkv, D)
     q = frame_qkv(cfg + 1000, pos, B, Hq, D)[0]
     return q, k, v
-
-
-def _vt_pos(key):
-    return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1)
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,W,D", [(2, 8, 2, 37, 64), (3, 4, 4, 16, 64), (1, 32, 1, 50, 32), (2, 6, 3, 1, 64)])
@@ -47,13 +43,13 @@ def test_decode_matches_oracle(B, Hq, Hkv, W, D):
     rows = (W + 64 + 63) // 64 * 64
     raw = dc.cache.view(torch.bfloat16).float().cpu().numpy()
     kb = raw[: B * Hkv * rows * D].reshape(B * Hkv, rows, D)
-    vb = raw[dc.nbytes // 4:][: B * Hkv * D * rows].reshape(B * Hkv, D, rows)
+    vb = vt_keys(raw[dc.nbytes // 4:][: B * Hkv * D * rows].reshape(B * Hkv, rows // 64, D, 64))
     last = 2 * W + 8
     for p in range(max(0, last - W + 1), last + 1):
         _, k, v = _token(40 + D, p, B, Hq, Hkv, D)
         s = p % W
         assert np.array_equal(kb[:, s, :], k.reshape(B * Hkv, D))
-        assert np.array_equal(vb[:, :, _vt_pos(s)], v.reshape(B * Hkv, D))
+        assert np.array_equal(vb[:, :, s], v.reshape(B * Hkv, D))
 
 
 def test_decode_full_window_sampled():

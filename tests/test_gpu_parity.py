@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import sliding_window_kv_amd as swa
-from gpu_helpers import (assert_close_bf16, assert_close_f32, bf16_round_f64, case, dev, host, lse_tol)
+from gpu_helpers import (assert_close_bf16, assert_close_f32, bf16_round_f64, case, dev, host, lse_tol, vt_keys)
 from oracle import (CacheConfig, NaiveRingCache, frame_visibility, masked_attention, prefill, rope3d,
                     token_mask)
 from swa_synth import chunk_qkv, frame_positions, frame_qkv
@@ -145,10 +145,7 @@ def test_cache_bytes_bit_exact():
     torch.cuda.synchronize()
     kr, vr = gc.region_views(0)
     K = kr.float().cpu().numpy()
-    # transposed V keeps key r at position r with bits 2 and 3 swapped
-    r = np.arange(vr.shape[2])
-    vt_pos = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1)
-    V = vr.float().cpu().numpy()[:, :, vt_pos]
+    V = vt_keys(vr.float().cpu().numpy())
     L = gc.layout
     for (f, region, slot, row0, nrows) in gc.pages():
         k, v = frames[f]
@@ -207,8 +204,7 @@ def test_specials_across_tile_boundaries():
     torch.cuda.synchronize()
     kr, vr = gc.region_views(0)
     K = kr.float().cpu().numpy()
-    r = np.arange(vr.shape[2])
-    V = vr.float().cpu().numpy()[:, :, (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1)]
+    V = vt_keys(vr.float().cpu().numpy())
     base = gc.layout.special_row_base
     specials = [p for p in gc.pages() if p[1] != swa.SWA_REGION_FRAME]
     assert len(specials) == R
