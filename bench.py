@@ -244,6 +244,18 @@ def bench_stream(args, torch, swa):
 
     append_bytes = 2 * 2 * P * H * D * 2
     ms_app = _device_ms(torch, app)
+    # The same attention call over a cache filled with zero frames and a zero
+    # query: the same kernel and instruction stream (every score 0, every
+    # probability 1), but the matrix and vector units switch far fewer bits.
+    # Timed last, so its launches are the last attention dispatches of the run.
+    zcache = swa.SwaCache(swa.make_config(P, H, D, sliding_window_size=W, scale_frames=S))
+    if args.splits is not None:
+        zcache.set_splits(args.splits)
+    zero = torch.zeros((P, H, D), dtype=torch.bfloat16, device="cuda")
+    for t in range(S + W + 1):
+        zcache.step(0, t, zero, zero, zero, True, out, None)
+    ms_attn_zero = _timed(torch, lambda _: zcache.attend(0, zero, out, None), args.steps)
+    del zcache
     res = _base(args, METRIC, flops / (ms_step * 1e-3) / 1e12, "TFLOP/s", ms_step,
                 {"workload": "stream_step", "tokens_per_frame": P, "heads": H, "head_dim": D, "scale_frames": S,
                  "window_frames": W, "visible_keys": keys, "splits": args.splits or "auto", "lse_output": False})
@@ -251,6 +263,7 @@ def bench_stream(args, torch, swa):
         "frames_per_s_per_layer": round(1000.0 / ms_step, 1),
         "attention_ms": round(ms_attn, 5),
         "attention_with_lse_ms": round(ms_attn_lse, 5),
+        "attention_ms_zero_inputs": round(ms_attn_zero, 5),
         "roofline": _mfma_roofline(flops, ms_attn, _measured_traffic("stream")),
         "append": _hbm_pass(append_bytes, ms_app, _copy_ceiling_gbs(torch, append_bytes)),
     })
@@ -438,6 +451,7 @@ def bench_rope(args, torch, swa):
     # the step minus its attention call: the fused RoPE + append pass, plus
     # host bookkeeping and launch gaps (kernel time alone: profiles/)
     res["rope_append_fused_bytes"] = 6 * P * H * D * 2
+    res["copy_ceiling_GBps_at_fused_size"] = round(_copy_ceiling_gbs(torch, 6 * P * H * D * 2), 1)
     res["step_minus_attention_us"] = round((ms - ms_attn) * 1e3, 2)
     if not args.no_cpu:
         from oracle import CacheConfig, NaiveRingCache, rope3d
