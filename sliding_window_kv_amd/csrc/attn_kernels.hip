@@ -456,6 +456,7 @@ struct Acc {
     f32x16 o[QB][D / 32];    // O^T accumulators
     float m[QB], l[QB];      // running max or offset (log2 domain) and row sum, per lane
     f32x16 c0[QB];           // offset softmax: score accumulator start, -m of the lane's query
+    bool live;               // the wave holds at least one query row (else it only loads and waits)
 };
 
 enum TileMode { kOnline = 0, kFirst = 1, kOffset = 2 };
@@ -590,7 +591,7 @@ __device__ __forceinline__ void ring_iter(int it, int ntiles, Cursor (&cq)[NB], 
         cq[NXT] = ld;
         tile_load<D, NW>(off, kh, vh, ld.base, kbuf[NXT], vbuf[NXT], wave);
     }
-    tile_step<D, QB, MODE, PRE>(kcur, vcur, cur, a, sl2, lane & 31, lane >> 5);
+    if (a.live) tile_step<D, QB, MODE, PRE>(kcur, vcur, cur, a, sl2, lane & 31, lane >> 5);
 }
 
 template <int D, int NW, int QB, int NB, int U, int MODE, bool PRE, class Src>
@@ -745,6 +746,7 @@ __device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<P
 
     const int qrow0 = qt * Sh::QROWS + wave * QB * 32;
     Acc<D, QB> a;
+    a.live = qrow0 < p.nq;       // waves past the frame's last row skip the arithmetic
     run_pass<D, NW, QB, true, PRE>(p, segs, frame, h, qrow0, t_begin, ntiles, off, kh, vh, KB, VB, a, tid);
     bool bad = false;
 #pragma unroll
