@@ -131,14 +131,17 @@ __device__ __forceinline__ void row_layer_norm(float (&x)[E], const float* w, co
     for (int e = 0; e < E; ++e) x[e] = fmaf(x[e] * inv, w[e], b[e]);
 }
 
-constexpr int kTileRows = 64;
+constexpr int kTileRows = 32;
 
-// Threads of an append block: one per 16-byte chunk of the block's 64 rows,
+// Threads of an append block: one per 16-byte chunk of the block's rows,
 // so that every thread has a single chunk of k, v (and q) to move and rotate.
 template <typename T, int D>
 constexpr int append_threads() { return kTileRows * D / Elt<T>::kPer16B; }
 
-// One block = 64 destination rows (64-aligned: one V^T block) of one head.
+// One block = 32 destination rows (32-aligned: half of one V^T block) of one
+// head.  (At the per-frame size a pass is bound by latency: 32-row blocks put
+// twice as many work-groups in flight as 64-row ones and measured faster,
+// 16-row ones slower.)
 template <typename T, int D, bool ROPE, bool NORM>
 __global__ __launch_bounds__((append_threads<T, D>())) void append_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                      T* __restrict__ kreg, T* __restrict__ vreg,
@@ -166,7 +169,7 @@ __global__ __launch_bounds__((append_threads<T, D>())) void append_kernel(const 
     __shared__ T vt[kTileRows * LD];
 
     const int h = blockIdx.y;
-    const int base = (row0 & ~63) + blockIdx.x * kTileRows;  // first destination row
+    const int base = (row0 & ~(kTileRows - 1)) + blockIdx.x * kTileRows;  // first destination row
     const int tid = threadIdx.x;
 
     if (meta_slot != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *meta_slot = frame_id;
@@ -412,9 +415,9 @@ hipError_t append_dispatch(int H, int n_tok, int row0, int rows, const void* k, 
                            void* kreg, void* vreg, void* q, const int32_t* pos, const RopeArgs* rope,
                            const NormArgs* norm, int32_t* meta_slot, int32_t frame_id, const RetainArgs& ret,
                            const StepPlan* plan, hipStream_t stream) {
-    const int first = row0 & ~63;
-    // with a device plan the first row is not known here: enough tiles for any 64-row offset
-    const int tiles = plan != nullptr ? (63 + n_tok + kTileRows - 1) / kTileRows
+    const int first = row0 & ~(kTileRows - 1);
+    // with a device plan the first row is not known here: enough tiles for any row offset
+    const int tiles = plan != nullptr ? (kTileRows - 1 + n_tok + kTileRows - 1) / kTileRows
                                       : (row0 + n_tok - first + kTileRows - 1) / kTileRows;
     dim3 grid(tiles, H);
     RopeArgs r{};
