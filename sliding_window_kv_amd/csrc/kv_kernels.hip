@@ -131,19 +131,19 @@ __device__ __forceinline__ void row_layer_norm(float (&x)[E], const float* w, co
     for (int e = 0; e < E; ++e) x[e] = fmaf(x[e] * inv, w[e], b[e]);
 }
 
-constexpr int kTileRows = 32;
+// Threads of an append block of TR rows: one per 16-byte chunk of the
+// block's rows, so that every thread has a single chunk of k, v (and q) to
+// move and rotate.
+template <typename T, int D, int TR>
+constexpr int append_threads() { return TR * D / Elt<T>::kPer16B; }
 
-// Threads of an append block: one per 16-byte chunk of the block's rows,
-// so that every thread has a single chunk of k, v (and q) to move and rotate.
-template <typename T, int D>
-constexpr int append_threads() { return kTileRows * D / Elt<T>::kPer16B; }
-
-// One block = 32 destination rows (32-aligned: half of one V^T block) of one
-// head.  (At the per-frame size a pass is bound by latency: 32-row blocks put
-// twice as many work-groups in flight as 64-row ones and measured faster,
-// 16-row ones slower.)
-template <typename T, int D, bool ROPE, bool NORM>
-__global__ __launch_bounds__((append_threads<T, D>())) void append_kernel(const T* __restrict__ k, const T* __restrict__ v,
+// One block = TR destination rows (TR-aligned, TR = 32 or 64: half of or one
+// whole V^T block) of one head.  A per-frame pass is bound by latency, and
+// 32-row blocks, with twice as many work-groups in flight, measured faster
+// there (16-row ones slower); a pass over many frames (the prefill's chunk
+// layout) has work-groups to spare and runs faster with 64-row blocks.
+template <typename T, int D, bool ROPE, bool NORM, int TR>
+__global__ __launch_bounds__((append_threads<T, D, TR>())) void append_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                      T* __restrict__ kreg, T* __restrict__ vreg,
                                                      T* __restrict__ q, const int32_t* __restrict__ pos,
                                                      RopeArgs rope, NormArgs norm, int H, int n_tok, int row0,
@@ -164,7 +164,8 @@ __global__ __launch_bounds__((append_threads<T, D>())) void append_kernel(const 
         frame_id = plan->frame;
     }
     constexpr int CPR = D / E;               // 16-byte chunks per row
-    constexpr int NT = append_threads<T, D>();
+    constexpr int NT = append_threads<T, D, TR>();
+    constexpr int kTileRows = TR;
     constexpr int LD = D + 2;                // padded LDS row
     __shared__ T vt[kTileRows * LD];
 
@@ -410,7 +411,7 @@ __global__ __launch_bounds__(256) void mask_kernel(int F, int P, int W, int S, i
     }
 }
 
-template <typename T, int D>
+template <typename T, int D, int kTileRows>
 hipError_t append_dispatch(int H, int n_tok, int row0, int rows, const void* k, const void* v,
                            void* kreg, void* vreg, void* q, const int32_t* pos, const RopeArgs* rope,
                            const NormArgs* norm, int32_t* meta_slot, int32_t frame_id, const RetainArgs& ret,
@@ -425,20 +426,41 @@ hipError_t append_dispatch(int H, int n_tok, int row0, int rows, const void* k, 
     NormArgs nm{};
     if (norm != nullptr) nm = *norm;
 #define SWA_APPEND(RO, NO)                                                                                  \
-    hipLaunchKernelGGL((append_kernel<T, D, RO, NO>), grid, dim3(append_threads<T, D>()), 0, stream,          \
+    hipLaunchKernelGGL((append_kernel<T, D, RO, NO, kTileRows>), grid, dim3(append_threads<T, D, kTileRows>()), \
+                       0, stream,                                                                         \
                        static_cast<const T*>(k),                                                          \
                        static_cast<const T*>(v), static_cast<T*>(kreg), static_cast<T*>(vreg), static_cast<T*>(q), \
                        pos, r, nm, H, n_tok, row0, rows, meta_slot, frame_id, ret, plan)
-    if (rope != nullptr && norm != nullptr)
-        SWA_APPEND(true, true);
-    else if (rope != nullptr)
-        SWA_APPEND(true, false);
-    else if (norm != nullptr)
-        SWA_APPEND(false, true);
-    else
+    if constexpr (kTileRows == 64) {
         SWA_APPEND(false, false);
+    } else {
+        if (rope != nullptr && norm != nullptr)
+            SWA_APPEND(true, true);
+        else if (rope != nullptr)
+            SWA_APPEND(true, false);
+        else if (norm != nullptr)
+            SWA_APPEND(false, true);
+        else
+            SWA_APPEND(false, false);
+    }
 #undef SWA_APPEND
     return hipGetLastError();
+}
+
+// 64-row blocks for plain (no RoPE, no norm) passes with at least 16
+// work-groups of 32 rows per CU's worth (4096 of them), 32-row blocks
+// otherwise.
+template <typename T, int D>
+hipError_t append_dispatch_any(int H, int n_tok, int row0, int rows, const void* k, const void* v, void* kreg,
+                               void* vreg, void* q, const int32_t* pos, const RopeArgs* rope, const NormArgs* norm,
+                               int32_t* meta_slot, int32_t frame_id, const RetainArgs& ret, const StepPlan* plan,
+                               hipStream_t stream) {
+    const bool big = rope == nullptr && norm == nullptr && (static_cast<int64_t>(n_tok) / 32) * H >= 4096;
+    if (big)
+        return append_dispatch<T, D, 64>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm, meta_slot,
+                                         frame_id, ret, plan, stream);
+    return append_dispatch<T, D, 32>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm, meta_slot,
+                                     frame_id, ret, plan, stream);
 }
 
 }  // namespace
@@ -449,15 +471,15 @@ hipError_t launch_append(int dtype, int H, int D, int n_tok, int row0, int rows,
                          const RetainArgs& ret, const StepPlan* plan, hipStream_t stream) {
     if (dtype == 0) {
         if (D == 64)
-            return append_dispatch<uint16_t, 64>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm,
+            return append_dispatch_any<uint16_t, 64>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm,
                                                  meta_slot, frame_id, ret, plan, stream);
-        return append_dispatch<uint16_t, 32>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm,
+        return append_dispatch_any<uint16_t, 32>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm,
                                              meta_slot, frame_id, ret, plan, stream);
     }
     if (D == 64)
-        return append_dispatch<float, 64>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm, meta_slot,
+        return append_dispatch_any<float, 64>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm, meta_slot,
                                           frame_id, ret, plan, stream);
-    return append_dispatch<float, 32>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm, meta_slot,
+    return append_dispatch_any<float, 32>(H, n_tok, row0, rows, k, v, kreg, vreg, q, pos, rope, norm, meta_slot,
                                       frame_id, ret, plan, stream);
 }
 
