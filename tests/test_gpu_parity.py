@@ -180,10 +180,11 @@ def test_stream_f32_specials_nonkey(sr0):
 
 def test_specials_across_tile_boundaries():
     # special rows 60..68 of a frame: in slot 0 they straddle the append's
-    # 64-row work-group boundary (each work-group retains the rows it is
-    # about to overwrite) and the 16-row V^T group boundary at 64; in slot 1
-    # (rows 210..218) they lie inside one work-group and inside the single
-    # V^T group [208, 224).  No scale frame, so both slots are reused.
+    # work-group boundary at row 64 (each work-group retains the rows it is
+    # about to overwrite), the 16-row V^T group boundary and the 64-key V^T
+    # block boundary there; in slot 1 (rows 210..218) they lie inside one
+    # work-group ([192, 224)) and inside the single V^T group [208, 224).
+    # No scale frame, so both slots are reused.
     # Outputs, pages and the retained bytes against the oracle.
     P, H, D, W, S, ns, R, sr0 = 150, 2, 64, 2, 0, 9, 3, 60
     case(f"specials at rows {sr0}..{sr0 + ns - 1}, P={P} W={W} R={R}")
