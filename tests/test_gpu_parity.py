@@ -424,6 +424,36 @@ def test_prefill_full_size_sampled():
         assert np.abs(gl[:, rows] - rl).max() <= lse_tol(int(vis[i].sum()) * P), f"lse frame {i}"
 
 
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("f32", 32), ("bf16", 32)])
+def test_prefill_large_chunk_layout(dtype, D):
+    # 8 frames x 1024 tokens x 16 heads: large enough (at least 4096
+    # work-groups of 32 rows) for the chunk layout to take 64-row append
+    # blocks, in the dtypes and head sizes the full-size prefill does not
+    # cover; sampled rows of three frames against the oracle.
+    F, P, H, W, S = 8, 1024, 16, 2, 1
+    case(f"prefill {dtype} D={D} F={F} P={P} H={H} (64-row layout blocks)")
+    f32 = dtype == "f32"
+    tdt = torch.float32 if f32 else torch.bfloat16
+    q, k, v = chunk_qkv(11, F, P, H, D, bf16=not f32)
+    out = torch.empty((F * P, H, D), dtype=tdt, device="cuda")
+    lse = torch.empty((H, F * P), dtype=torch.float32, device="cuda")
+    swa.prefill_t(dev(q, tdt), dev(k, tdt), dev(v, tdt), F, P, W, 1, S, out, lse)
+    got, gl = host(out), host(lse)
+    vis = frame_visibility(F, W, 1, S)
+    fk = np.arange(F * P) // P
+    sample = np.array([0, 1, 31, 32, 63, 64, 500, 1023])
+    for i in (0, 3, 7):
+        rows = i * P + sample
+        mask = np.broadcast_to(vis[i][fk][None, :], (len(rows), F * P))
+        ro, rl = masked_attention(q[rows], k, v, mask)
+        if f32:
+            assert_close_f32(got[rows], ro, f"frame {i}")
+            assert_close_f32(gl[:, rows], rl, f"lse frame {i}")
+        else:
+            assert_close_bf16(got[rows], ro, f"frame {i}")
+            assert np.abs(gl[:, rows] - rl).max() <= lse_tol(int(vis[i].sum()) * P), f"lse frame {i}"
+
+
 # ---------------------------------------------------------------------------
 # the offset softmax's recompute with a running max
 # ---------------------------------------------------------------------------
