@@ -547,13 +547,17 @@ __device__ __forceinline__ void tile_step(const uint16_t* ks, const uint16_t* vs
 
 // Work-group barrier after this wave's LDS accesses and all but its N
 // youngest vector-memory operations have completed (loads return in order,
-// so the older direct-to-LDS tiles have landed).  Written out rather than
-// __syncthreads(): the fences of that one made the compiler wait for every
-// load in flight, the prefetched tiles included.
+// so the older direct-to-LDS tiles have landed).  Not __syncthreads(): its
+// fences made the compiler wait for every load in flight, the prefetched
+// tiles included.  The wait is the builtin, not inline assembly, so that
+// the compiler's own wait counting knows the older tiles have landed and
+// adds no wait for all loads before the next LDS reads.
 template <int N>
 __device__ __forceinline__ void sync_tiles() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+    // s_waitcnt vmcnt(N) expcnt(7) lgkmcnt(0): vmcnt in bits 3:0 and 15:14
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);           // no instruction moves across the barrier
 }
 
@@ -565,7 +569,11 @@ __device__ __forceinline__ void sync_tiles() {
 // it + NB - 1, then compute.  U is a compile-time constant and every buffer
 // is an LDS variable of its own, so the compiler can tell the buffer being
 // read from the ones being loaded (with one array it waited for all loads).
-template <int D, int NW, int QB, int NB, int U, int MODE, bool PRE, class Src>
+// FULL: every tile this iteration waits for or loads exists, so the load is
+// unconditional; loops of such iterations have no branch around a tile load,
+// across which the compiler's wait counting would again fall back to
+// waiting for all loads in flight.
+template <int D, int NW, int QB, int NB, int U, int MODE, bool PRE, bool FULL = false, class Src>
 __device__ __forceinline__ void ring_iter(int it, int ntiles, Cursor (&cq)[NB], Cursor& ld, const Src& segs,
                                           const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
                                           uint16_t* const (&kbuf)[kMaxBufs], uint16_t* const (&vbuf)[kMaxBufs],
@@ -575,7 +583,7 @@ __device__ __forceinline__ void ring_iter(int it, int ntiles, Cursor (&cq)[NB], 
     constexpr int NXT = (U + NB - 1) % NB;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS destinations stay scalar
-    if (it + NB - 2 < ntiles)
+    if (FULL || it + NB - 2 < ntiles)
         sync_tiles<(NB - 2) * PER_TILE>();
     else
         sync_tiles<0>();
@@ -586,7 +594,7 @@ __device__ __forceinline__ void ring_iter(int it, int ntiles, Cursor (&cq)[NB], 
         tile_clear_edges<D, NW * 64>(vcur, cur, tid);
         sync_tiles<63>();
     }
-    if (it + NB - 1 < ntiles) {
+    if (FULL || it + NB - 1 < ntiles) {
         cursor_next(segs, &ld);
         cq[NXT] = ld;
         tile_load<D, NW>(off, kh, vh, ld.base, kbuf[NXT], vbuf[NXT], wave);
@@ -607,14 +615,14 @@ __device__ __forceinline__ void ring_tail(int it, int ntiles, Cursor (&cq)[NB], 
     }
 }
 
-template <int D, int NW, int QB, int NB, int U, int MODE, bool PRE, class Src>
+template <int D, int NW, int QB, int NB, int U, int MODE, bool PRE, bool FULL, class Src>
 __device__ __forceinline__ void ring_round(int it, int ntiles, Cursor (&cq)[NB], Cursor& ld, const Src& segs,
                                            const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
                                            uint16_t* const (&kbuf)[kMaxBufs], uint16_t* const (&vbuf)[kMaxBufs],
                                            Acc<D, QB>& a, float sl2, int tid) {
     if constexpr (U < NB) {
-        ring_iter<D, NW, QB, NB, U, MODE, PRE>(it + U, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, a, sl2, tid);
-        ring_round<D, NW, QB, NB, U + 1, MODE, PRE>(it, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, a, sl2, tid);
+        ring_iter<D, NW, QB, NB, U, MODE, PRE, FULL>(it + U, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, a, sl2, tid);
+        ring_round<D, NW, QB, NB, U + 1, MODE, PRE, FULL>(it, ntiles, cq, ld, segs, off, kh, vh, kbuf, vbuf, a, sl2, tid);
     }
 }
 
@@ -700,13 +708,18 @@ __device__ __forceinline__ void run_pass(const AttnParams& p, const Src& segs, i
         ring_iter<D, NW, QB, NB, 0, kFirst, PRE>(0, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
         ring_tail<D, NW, QB, NB, 1, kOffset, PRE>(1, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
         int it = NB;
+        // rounds whose loads all exist, then at most one round with guarded loads
+        for (; it + 2 * NB - 1 <= ntiles; it += NB)
+            ring_round<D, NW, QB, NB, 0, kOffset, PRE, true>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
         for (; it + NB <= ntiles; it += NB)
-            ring_round<D, NW, QB, NB, 0, kOffset, PRE>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
+            ring_round<D, NW, QB, NB, 0, kOffset, PRE, false>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
         ring_tail<D, NW, QB, NB, 0, kOffset, PRE>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
     } else {
         int it = 0;
+        for (; it + 2 * NB - 1 <= ntiles; it += NB)
+            ring_round<D, NW, QB, NB, 0, kOnline, false, true>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
         for (; it + NB <= ntiles; it += NB)
-            ring_round<D, NW, QB, NB, 0, kOnline, false>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
+            ring_round<D, NW, QB, NB, 0, kOnline, false, false>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
         ring_tail<D, NW, QB, NB, 0, kOnline, false>(it, ntiles, cq, ld, segs, off, kh, vh, KB, VB, a, sl2, tid);
     }
 }
