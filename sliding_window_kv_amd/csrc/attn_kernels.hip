@@ -15,7 +15,7 @@
 //    operand of v_mfma_f32_32x32x16_bf16.
 //  * Keys stream through LDS in 64-aligned tiles of 64 rows, in a ring of
 //    kRing buffers (kRing - 1 tiles in flight while one is consumed), loaded
-//    with direct global->LDS 16-byte loads (no staging registers).  A tile
+//    with direct buffer->LDS 16-byte loads (no staging registers).  A tile
 //    is a contiguous 64 x D block of K rows and, with V^T stored in blocks of
 //    64 keys, a contiguous [D][64] block of V^T; in LDS both are kept in that
 //    shape with 16-byte chunks XOR-swizzled by row, so the MFMA operand reads
@@ -248,11 +248,11 @@ __device__ __forceinline__ void write_out(const AttnParams& p, const f32x16 (&o)
     }
 }
 
-// Per-lane element offsets of the 16-byte chunks a thread loads into one
-// K tile ([64][D], swizzled) and one V^T tile ([D][64], swizzled) from the
+// Per-lane byte offsets of the 16-byte chunks a thread loads into one K
+// tile ([64][D], swizzled) and one V^T tile ([D][64], swizzled) from the
 // tile's K rows and V^T block, each contiguous and starting at element
-// base * D of its head's region: every load is that uniform base plus one
-// of these constant offsets.
+// base * D of its head's region: every load is that uniform offset plus one
+// of these constant ones.
 template <int D, int NW>
 struct TileOffsets {
     static constexpr int CPR = D / 8;
@@ -265,36 +265,34 @@ struct TileOffsets {
         for (int i = 0; i < NK; ++i) {
             const int p = (i * NW + wave) * 64 + lane;
             const int row = p / CPR;
-            k[i] = row * D + ((p % CPR) ^ lds_swz<CPR>(row)) * 8;
+            k[i] = (row * D + ((p % CPR) ^ lds_swz<CPR>(row)) * 8) * 2;
         }
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int p = (i * NW + wave) * 64 + lane;
             const int d = p / 8;
-            v[i] = d * KT + ((p % 8) ^ lds_swz<8>(d)) * 8;
+            v[i] = (d * KT + ((p % 8) ^ lds_swz<8>(d)) * 8) * 2;
         }
     }
 };
 
 // Direct global->LDS loads of the 64-key tile starting at row `base`.
 template <int D, int NW>
-__device__ __forceinline__ void tile_load(const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
+__device__ __forceinline__ void tile_load(const TileOffsets<D, NW>& off, __amdgpu_buffer_rsrc_t kh, __amdgpu_buffer_rsrc_t vh,
                                           int base, uint16_t* ks, uint16_t* vs, int wave) {
     using TO = TileOffsets<D, NW>;
-    // scalar base + unsigned 32-bit byte offset: the loads take the
-    // SGPR-base form and need no per-load 64-bit address arithmetic
-    const char* kt = reinterpret_cast<const char*>(kh + static_cast<size_t>(base) * D);
-    const char* vt = reinterpret_cast<const char*>(vh + static_cast<size_t>(base) * D);
+    // buffer loads: the tile's byte offset in a scalar, the lane's in a
+    // vector register, so no load needs 64-bit address arithmetic (which the
+    // global form took per load)
+    const uint32_t sb = static_cast<uint32_t>(base) * (D * 2u);
 #pragma unroll
     for (int i = 0; i < TO::NK; ++i)
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(kt + static_cast<uint32_t>(off.k[i]) * 2u),
-            (__attribute__((address_space(3))) void*)(ks + (i * NW + wave) * 512), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kh, (__attribute__((address_space(3))) void*)(ks + (i * NW + wave) * 512),
+                                                 16, static_cast<uint32_t>(off.k[i]), sb, 0, 0);
 #pragma unroll
     for (int i = 0; i < TO::NV; ++i)
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(vt + static_cast<uint32_t>(off.v[i]) * 2u),
-            (__attribute__((address_space(3))) void*)(vs + (i * NW + wave) * 512), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vh, (__attribute__((address_space(3))) void*)(vs + (i * NW + wave) * 512),
+                                                 16, static_cast<uint32_t>(off.v[i]), sb, 0, 0);
 }
 
 // The three phases of one 64-key tile for one wave.  LDS reads address a
@@ -575,7 +573,7 @@ __device__ __forceinline__ void sync_tiles() {
 // waiting for all loads in flight.
 template <int D, int NW, int QB, int NB, int U, int MODE, bool PRE, bool FULL = false, class Src>
 __device__ __forceinline__ void ring_iter(int it, int ntiles, Cursor (&cq)[NB], Cursor& ld, const Src& segs,
-                                          const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
+                                          const TileOffsets<D, NW>& off, __amdgpu_buffer_rsrc_t kh, __amdgpu_buffer_rsrc_t vh,
                                           uint16_t* const (&kbuf)[kMaxBufs], uint16_t* const (&vbuf)[kMaxBufs],
                                           Acc<D, QB>& a, float sl2, int tid) {
     using TO = TileOffsets<D, NW>;
@@ -604,7 +602,7 @@ __device__ __forceinline__ void ring_iter(int it, int ntiles, Cursor (&cq)[NB], 
 
 template <int D, int NW, int QB, int NB, int U, int MODE, bool PRE, class Src>
 __device__ __forceinline__ void ring_tail(int it, int ntiles, Cursor (&cq)[NB], Cursor& ld, const Src& segs,
-                                          const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
+                                          const TileOffsets<D, NW>& off, __amdgpu_buffer_rsrc_t kh, __amdgpu_buffer_rsrc_t vh,
                                           uint16_t* const (&kbuf)[kMaxBufs], uint16_t* const (&vbuf)[kMaxBufs],
                                           Acc<D, QB>& a, float sl2, int tid) {
     if constexpr (U < NB) {
@@ -617,7 +615,7 @@ __device__ __forceinline__ void ring_tail(int it, int ntiles, Cursor (&cq)[NB], 
 
 template <int D, int NW, int QB, int NB, int U, int MODE, bool PRE, bool FULL, class Src>
 __device__ __forceinline__ void ring_round(int it, int ntiles, Cursor (&cq)[NB], Cursor& ld, const Src& segs,
-                                           const TileOffsets<D, NW>& off, const uint16_t* kh, const uint16_t* vh,
+                                           const TileOffsets<D, NW>& off, __amdgpu_buffer_rsrc_t kh, __amdgpu_buffer_rsrc_t vh,
                                            uint16_t* const (&kbuf)[kMaxBufs], uint16_t* const (&vbuf)[kMaxBufs],
                                            Acc<D, QB>& a, float sl2, int tid) {
     if constexpr (U < NB) {
@@ -671,8 +669,8 @@ __device__ __forceinline__ void load_q(const AttnParams& p, int frame, int h, in
 // softmax (OFFSET = true; PRE: with Q pre-scaled).
 template <int D, int NW, int QB, bool OFFSET, bool PRE, class Src>
 __device__ __forceinline__ void run_pass(const AttnParams& p, const Src& segs, int frame, int h, int qrow0,
-                                         int t_begin, int ntiles, const TileOffsets<D, NW>& off, const uint16_t* kh,
-                                         const uint16_t* vh, uint16_t* const (&KB)[kMaxBufs],
+                                         int t_begin, int ntiles, const TileOffsets<D, NW>& off, __amdgpu_buffer_rsrc_t kh,
+                                         __amdgpu_buffer_rsrc_t vh, uint16_t* const (&KB)[kMaxBufs],
                                          uint16_t* const (&VB)[kMaxBufs], Acc<D, QB>& a, int tid) {
     constexpr int NB = kRing;
     const int lane = tid & 63;
@@ -742,8 +740,15 @@ __device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<P
     const int hl = lane >> 5;
     const int ntiles = t_end - t_begin;
 
-    const uint16_t* kh = static_cast<const uint16_t*>(p.kreg) + static_cast<size_t>(h) * p.rows * D;
-    const uint16_t* vh = static_cast<const uint16_t*>(p.vreg) + static_cast<size_t>(h) * D * p.rows;
+    const uint16_t* kp = static_cast<const uint16_t*>(p.kreg) + static_cast<size_t>(h) * p.rows * D;
+    const uint16_t* vp = static_cast<const uint16_t*>(p.vreg) + static_cast<size_t>(h) * D * p.rows;
+    // one head's K rows and V^T blocks as raw buffer resources: stride 0,
+    // the region's bytes as the record count, 32-bit data format (word 3)
+    constexpr int kRawBuffer = 0x00020000;
+    const __amdgpu_buffer_rsrc_t kh =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kp), 0, p.rows * D * 2, kRawBuffer);
+    const __amdgpu_buffer_rsrc_t vh =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vp), 0, p.rows * D * 2, kRawBuffer);
     const TileOffsets<D, NW> off(wave, lane);
 
     if constexpr (!PREFILL && NW == 1) {
