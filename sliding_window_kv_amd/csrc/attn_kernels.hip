@@ -349,8 +349,8 @@ __device__ __forceinline__ void tile_scores(const uint16_t* ks, const bf16x8 (&q
 // Keys outside the tile's segment get score -inf (rare path: tiles at
 // segment edges).
 template <int QB>
-__device__ __forceinline__ void tile_mask(f32x16 (&s)[2][QB], const Cursor& cur, int hl) {
-    if (cur.base < cur.lo || cur.base + KT > cur.hi) {
+__device__ __forceinline__ void tile_mask(f32x16 (&s)[2][QB], const Cursor& cur, int hl, int edge) {
+    if (edge) {
         // its 32 per-lane key offsets must not be hoisted into registers
         // held across the whole loop
         int hx = hl;
@@ -375,10 +375,10 @@ __device__ __forceinline__ void tile_mask(f32x16 (&s)[2][QB], const Cursor& cur,
 template <int D, int QB>
 __device__ __forceinline__ void tile_softmax(f32x16 (&s)[2][QB], const Cursor& cur, bf16x8 (&pb)[2][QB][2],
                                              f32x16 (&o)[QB][D / 32], float (&m)[QB], float (&l)[QB], float sl2,
-                                             int hl) {
+                                             int hl, int edge) {
     constexpr int DB = D / 32;
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-    tile_mask<QB>(s, cur, hl);
+    tile_mask<QB>(s, cur, hl, edge);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         float mx = s[0][qb][0];
@@ -454,7 +454,8 @@ struct Acc {
     f32x16 o[QB][D / 32];    // O^T accumulators
     float m[QB], l[QB];      // running max or offset (log2 domain) and row sum, per lane
     f32x16 c0[QB];           // offset softmax: score accumulator start, -m of the lane's query
-    bool live;               // the wave holds at least one query row (else it only loads and waits)
+    int live;                // nonzero: the wave holds at least one query row (else it only loads and waits)
+    int wave;                // the wave's index in the work-group (uniform)
 };
 
 enum TileMode { kOnline = 0, kFirst = 1, kOffset = 2 };
@@ -523,21 +524,21 @@ __device__ __forceinline__ void tile_first_offset(f32x16 (&s)[2][QB], float (&m)
 // score product); otherwise Q exact and the exponent one FMA.
 template <int D, int QB, int MODE, bool PRE>
 __device__ __forceinline__ void tile_step(const uint16_t* ks, const uint16_t* vs, const Cursor& cur, Acc<D, QB>& a,
-                                          float sl2, int l32, int hl) {
+                                          float sl2, int l32, int hl, int edge) {
     f32x16 s[2][QB];
     bf16x8 pb[2][QB][2];
     const TileLanes<D> tl(l32, hl);
     if constexpr (MODE == kOnline) {
         tile_scores<D, QB, true>(ks, a.qf, s, tl, a.c0);
-        tile_softmax<D, QB>(s, cur, pb, a.o, a.m, a.l, sl2, hl);
+        tile_softmax<D, QB>(s, cur, pb, a.o, a.m, a.l, sl2, hl, edge);
     } else if constexpr (MODE == kFirst) {
         tile_scores<D, QB, true>(ks, a.qf, s, tl, a.c0);
-        tile_mask<QB>(s, cur, hl);
+        tile_mask<QB>(s, cur, hl, edge);
         tile_first_offset<QB, PRE>(s, a.m, a.c0, sl2);
         tile_exp<QB, !PRE>(s, pb, a.l, a.m, sl2);
     } else {
         tile_scores<D, QB, !PRE>(ks, a.qf, s, tl, a.c0);
-        tile_mask<QB>(s, cur, hl);
+        tile_mask<QB>(s, cur, hl, edge);
         tile_exp<QB, !PRE>(s, pb, a.l, a.m, sl2);
     }
     tile_pv<D, QB>(vs, pb, a.o, tl);
@@ -580,7 +581,7 @@ __device__ __forceinline__ void ring_iter(int it, int ntiles, Cursor (&cq)[NB], 
     constexpr int PER_TILE = TO::NK + TO::NV;    // load instructions per wave per tile
     constexpr int NXT = (U + NB - 1) % NB;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS destinations stay scalar
+    const int wave = a.wave;
     if (FULL || it + NB - 2 < ntiles)
         sync_tiles<(NB - 2) * PER_TILE>();
     else
@@ -588,7 +589,10 @@ __device__ __forceinline__ void ring_iter(int it, int ntiles, Cursor (&cq)[NB], 
     const Cursor cur = cq[U];
     uint16_t* kcur = kbuf[U];
     uint16_t* vcur = vbuf[U];
-    if (cur.base < cur.lo || cur.base + KT > cur.hi) {
+    // uniform flag in a scalar register (else it travels to the masking in
+    // tile_step as a per-lane boolean)
+    const int edge = __builtin_amdgcn_readfirstlane((cur.base < cur.lo || cur.base + KT > cur.hi) ? 1 : 0);
+    if (edge) {
         tile_clear_edges<D, NW * 64>(vcur, cur, tid);
         sync_tiles<63>();
     }
@@ -597,7 +601,7 @@ __device__ __forceinline__ void ring_iter(int it, int ntiles, Cursor (&cq)[NB], 
         cq[NXT] = ld;
         tile_load<D, NW>(off, kh, vh, ld.base, kbuf[NXT], vbuf[NXT], wave);
     }
-    if (a.live) tile_step<D, QB, MODE, PRE>(kcur, vcur, cur, a, sl2, lane & 31, lane >> 5);
+    if (a.live) tile_step<D, QB, MODE, PRE>(kcur, vcur, cur, a, sl2, lane & 31, lane >> 5, edge);
 }
 
 template <int D, int NW, int QB, int NB, int U, int MODE, bool PRE, class Src>
@@ -764,7 +768,8 @@ __device__ __forceinline__ void attend_range(const AttnParams& p, const SegSrc<P
 
     const int qrow0 = qt * Sh::QROWS + wave * QB * 32;
     Acc<D, QB> a;
-    a.live = qrow0 < p.nq;       // waves past the frame's last row skip the arithmetic
+    a.live = __builtin_amdgcn_readfirstlane(qrow0 < p.nq ? 1 : 0);
+    a.wave = wave;   // waves past the frame's last row skip the arithmetic
     run_pass<D, NW, QB, true, PRE>(p, segs, frame, h, qrow0, t_begin, ntiles, off, kh, vh, KB, VB, a, tid);
     bool bad = false;
 #pragma unroll
