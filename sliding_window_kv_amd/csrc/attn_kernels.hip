@@ -276,7 +276,7 @@ struct TileOffsets {
     }
 };
 
-// Direct global->LDS loads of the 64-key tile starting at row `base`.
+// Direct buffer->LDS loads of the 64-key tile starting at row `base`.
 template <int D, int NW>
 __device__ __forceinline__ void tile_load(const TileOffsets<D, NW>& off, __amdgpu_buffer_rsrc_t kh, __amdgpu_buffer_rsrc_t vh,
                                           int base, uint16_t* ks, uint16_t* vs, int wave) {
