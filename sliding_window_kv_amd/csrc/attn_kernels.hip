@@ -591,7 +591,7 @@ __device__ __forceinline__ void ring_iter(int it, int ntiles, Cursor (&cq)[NB], 
     uint16_t* vcur = vbuf[U];
     // uniform flag in a scalar register (else it travels to the masking in
     // tile_step as a per-lane boolean)
-    const int edge = __builtin_amdgcn_readfirstlane((cur.base < cur.lo || cur.base + KT > cur.hi) ? 1 : 0);
+    const int edge = ((cur.base - cur.lo) | (cur.hi - cur.base - KT)) >> 31;   // -1: an edge tile, 0: interior
     if (edge) {
         tile_clear_edges<D, NW * 64>(vcur, cur, tid);
         sync_tiles<63>();
