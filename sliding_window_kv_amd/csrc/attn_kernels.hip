@@ -919,41 +919,32 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     if (lse != nullptr && chunk == 0) lse[static_cast<size_t>(h) * nq + r] = (M + log2f(Lsum)) * 0.69314718055994530942f;
 }
 
-// Merge for few query rows and many pieces per head (token decode): one
-// work-group per head.  Per row, one wave reduces the pieces' maxima and
-// sums across its lanes and leaves the normalised weights in LDS; then the
-// threads split the (row, 4-feature chunk) items and, when there are fewer
-// items than threads, the pieces too, reducing through LDS.
-constexpr int kWideWeights = 8192;          // nq * pieces per head held in LDS
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-    return x;
-}
+// Merge for few query rows and many pieces per head (token decode).  Each
+// (row, 4-feature chunk) item gets 16 lanes of one wave, which split the
+// head's pieces; a lane loads a batch of its pieces at once, folds them with
+// its own maximum, and the 16 lanes then combine their (max, sum, output)
+// triples through cross-lane exchanges: no LDS and no barrier, and for up
+// to 128 pieces per head a single round of loads.
+constexpr int kDecodeLanes = 16;            // lanes per item
+constexpr int kDecodeBatch = 8;             // pieces per lane loaded at once
 
 template <int D>
-__global__ __launch_bounds__(256) void merge_wide_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                                                         uint16_t* __restrict__ out, float* __restrict__ lse, int H,
-                                                         int nq, int n, int ncols, int64_t rs, int64_t hs,
-                                                         const int* __restrict__ dn) {
+__global__ __launch_bounds__(256) void merge_decode_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_ml,
+                                                           uint16_t* __restrict__ out, float* __restrict__ lse, int H,
+                                                           int nq, int n, int ncols, int64_t rs, int64_t hs,
+                                                           const int* __restrict__ dn) {
     constexpr int C = D / 4;
+    constexpr int IPB = 256 / kDecodeLanes;          // items per work-group
     if (dn != nullptr) {                             // captured step: tile count from device memory
         n = *dn;
         ncols = static_cast<int64_t>(H) * n < ncols ? H * n : ncols;
     }
-    __shared__ float wts[kWideWeights];
-    __shared__ f32x4 red[256];
-    const int h = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int items = nq * C;
+    const int blocks_per_head = (items + IPB - 1) / IPB;
+    const int h = blockIdx.x / blocks_per_head;
+    const int item = (blockIdx.x % blocks_per_head) * IPB + threadIdx.x / kDecodeLanes;
+    const int pl = threadIdx.x % kDecodeLanes;
     const int64_t hn = static_cast<int64_t>(H) * n;
     const int64_t a = static_cast<int64_t>(h) * n;
     const int c_lo = column_of(a, hn, ncols);
@@ -961,59 +952,68 @@ __global__ __launch_bounds__(256) void merge_wide_kernel(const float* __restrict
     if (c_lo == c_hi) return;                       // whole head in one column: written by the attention kernel
     const int npc = c_hi - c_lo + 1;
     const int first = 2 * c_lo + (hn * c_lo / ncols >= a ? 0 : 1);   // see merge_kernel
-    auto piece_of = [&](int j) { return j == 0 ? first : 2 * (c_lo + j); };
-    for (int r = wave; r < nq; r += 4) {
-        float M = -INFINITY;
-        for (int j = lane; j < npc; j += 64)
-            M = fmaxf(M, part_ml[(static_cast<size_t>(piece_of(j)) * nq + r) * 2]);
-        M = wave_max(M);
-        float Ls = 0.f;
-        for (int j = lane; j < npc; j += 64) {
-            const size_t row = static_cast<size_t>(piece_of(j)) * nq + r;
-            const float ms = part_ml[row * 2];
-            const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-            Ls += w * part_ml[row * 2 + 1];
-            wts[r * npc + j] = w;
+    // lanes past the last item load item 0's data and take part in the
+    // exchanges, but store nothing
+    const bool ok = item < items;
+    const int r = ok ? item / C : 0;
+    const int chunk = ok ? item % C : 0;
+    float M = -INFINITY;
+    float Ls = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = pl; j0 < npc; j0 += kDecodeLanes * kDecodeBatch) {
+        float ms[kDecodeBatch], ls[kDecodeBatch];
+        f32x4 oc[kDecodeBatch];
+#pragma unroll
+        for (int u = 0; u < kDecodeBatch; ++u) {
+            const int j = j0 + u * kDecodeLanes;
+            if (j < npc) {
+                const int piece = j == 0 ? first : 2 * (c_lo + j);
+                const size_t row = static_cast<size_t>(piece) * nq + r;
+                ms[u] = part_ml[row * 2];
+                ls[u] = part_ml[row * 2 + 1];
+                oc[u] = *reinterpret_cast<const f32x4*>(part_o + row * D + chunk * 4);
+            } else {
+                ms[u] = -INFINITY;
+                ls[u] = 0.f;
+                oc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
-        Ls = wave_sum(Ls);
-        const float inv = 1.f / Ls;
-        for (int j = lane; j < npc; j += 64) wts[r * npc + j] *= inv;
-        if (lse != nullptr && lane == 0)
-            lse[static_cast<size_t>(h) * nq + r] = (M + log2f(Ls)) * 0.69314718055994530942f;
+        float mb = M;
+#pragma unroll
+        for (int u = 0; u < kDecodeBatch; ++u) mb = fmaxf(mb, ms[u]);
+        if (mb > M) {
+            const float scale = __builtin_amdgcn_exp2f(M - mb);     // 0 while M = -inf
+            Ls *= scale;
+            acc *= scale;
+            M = mb;
+        }
+#pragma unroll
+        for (int u = 0; u < kDecodeBatch; ++u) {
+            const float w = ms[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[u] - M);
+            Ls += w * ls[u];
+            acc += w * oc[u];
+        }
     }
-    __syncthreads();
-    const int items = nq * C;
-    int PG = 1;                                     // piece groups per item (power of 2)
-    while (PG * 2 * items <= 256) PG *= 2;
-    for (int i0 = 0; i0 < items; i0 += 256 / PG) {
-        const int item = i0 + tid % (256 / PG);
-        const int pg = tid / (256 / PG);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const bool ok = item < items;
-        if (ok) {
-            const int r = item / C;
-            const int chunk = item % C;
-            // unrolled so that several pieces' loads are in flight at once
-#pragma unroll 4
-            for (int j = pg; j < npc; j += PG) {
-                const size_t row = static_cast<size_t>(piece_of(j)) * nq + r;
-                acc += wts[r * npc + j] * *reinterpret_cast<const f32x4*>(part_o + row * D + chunk * 4);
-            }
-        }
-        if (PG > 1) {
-            red[tid] = acc;
-            __syncthreads();
-            if (pg == 0) {
-                for (int g = 1; g < PG; ++g) acc += red[tid + g * (256 / PG)];
-            }
-            __syncthreads();
-        }
-        if (ok && pg == 0) {
-            const int r = item / C;
-            const int chunk = item % C;
-            const int64_t g = r * rs + h * hs + chunk * 4;
-            *reinterpret_cast<u32x2*>(out + g) = u32x2{pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3])};
-        }
+    // the item's 16 lanes are consecutive: exchanges with lane ^ 8, 4, 2, 1
+    float Mg = M;
+#pragma unroll
+    for (int off = kDecodeLanes / 2; off >= 1; off >>= 1) Mg = fmaxf(Mg, __shfl_xor(Mg, off));
+    const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mg);
+    Ls *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int off = kDecodeLanes / 2; off >= 1; off >>= 1) {
+        Ls += __shfl_xor(Ls, off);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[k] += __shfl_xor(acc[k], off);
+    }
+    if (ok && pl == 0) {
+        const float inv = 1.f / Ls;
+        const int64_t g = r * rs + h * hs + chunk * 4;
+        *reinterpret_cast<u32x2*>(out + g) =
+            u32x2{pack_bf2(acc[0] * inv, acc[1] * inv), pack_bf2(acc[2] * inv, acc[3] * inv)};
+        if (lse != nullptr && chunk == 0)
+            lse[static_cast<size_t>(h) * nq + r] = (Mg + log2f(Ls)) * 0.69314718055994530942f;
     }
 }
 
@@ -1168,13 +1168,14 @@ hipError_t launch_attention(int dtype, int D, bool prefill, const AttnParams& p,
 
 hipError_t launch_merge(int D, int H, int nq, int n, int ncols, const float* part_o, const float* part_ml, void* out,
                         float* lse, int64_t rs, int64_t hs, const int* dn, hipStream_t stream) {
-    // pieces per head are at most ncols / H + 2
-    if (nq <= 32 && static_cast<int64_t>(nq) * (ncols / H + 2) <= kWideWeights) {
+    if (nq <= 32) {
+        const int64_t ipb = 256 / kDecodeLanes;
+        const int64_t blocks = static_cast<int64_t>(H) * ((static_cast<int64_t>(nq) * (D / 4) + ipb - 1) / ipb);
         if (D == 64)
-            hipLaunchKernelGGL((merge_wide_kernel<64>), dim3(H), dim3(256), 0, stream, part_o, part_ml,
+            hipLaunchKernelGGL((merge_decode_kernel<64>), dim3(blocks), dim3(256), 0, stream, part_o, part_ml,
                                static_cast<uint16_t*>(out), lse, H, nq, n, ncols, rs, hs, dn);
         else
-            hipLaunchKernelGGL((merge_wide_kernel<32>), dim3(H), dim3(256), 0, stream, part_o, part_ml,
+            hipLaunchKernelGGL((merge_decode_kernel<32>), dim3(blocks), dim3(256), 0, stream, part_o, part_ml,
                                static_cast<uint16_t*>(out), lse, H, nq, n, ncols, rs, hs, dn);
         return hipGetLastError();
     }
