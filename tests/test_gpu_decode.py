@@ -69,3 +69,28 @@ def test_decode_full_window_sampled():
             ro, rl = oc.attend(pos, q[0])
             assert_close_bf16(host(out)[0], ro, f"pos={pos}")
             assert np.abs(host(lse)[0] - rl).max() <= lse_tol(min(pos + 1, W))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,W,D", [(1, 3, 1, 12000, 32), (2, 6, 2, 9000, 64)])
+def test_decode_long_window_many_pieces(B, Hq, Hkv, W, D):
+    # more than 128 key tiles per buffer, so the merge folds its pieces in
+    # more than one batch per lane; three query heads per kv head leave part
+    # of the merge's last work-group without an item
+    case(f"decode long window B={B} Hq={Hq} Hkv={Hkv} W={W} D={D}")
+    dc = swa.DecodeCache(B, Hq, Hkv, W, D)
+    oc = [RollingDecodeCache(W, Hkv, D) for _ in range(B)]
+    check = {0, 130 * 64 - 1, W - 1, W, W + 77}
+    toks = [_token(60 + D, i, B, Hq, Hkv, D) for i in range(389)]   # position p draws token p mod 389
+    dtoks = [tuple(dev(x) for x in t) for t in toks]
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    for pos in range(W + 78):
+        q, k, v = toks[pos % 389]
+        dc.step(pos, *dtoks[pos % 389], out, lse)
+        for b in range(B):
+            oc[b].append(pos, k[b], v[b])
+        if pos in check:
+            for b in range(B):
+                ro, rl = oc[b].attend(pos, q[b])
+                assert_close_bf16(host(out)[b], ro, f"pos={pos} b={b}")
+                assert np.abs(host(lse)[b] - rl).max() <= lse_tol(min(pos + 1, W)), f"lse pos={pos} b={b}"
