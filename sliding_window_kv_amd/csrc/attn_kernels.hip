@@ -27,10 +27,15 @@
 //    directly as the B operand of O^T = V^T P^T: the key order inside each
 //    16-key step follows the accumulator layout, and V^T is stored with that
 //    order (vt_pos), so each lane's A operand is one 16-byte LDS read.
-//  * Online softmax in the log2 domain (scores scaled by log2(e)/sqrt(D));
-//    the row sum is taken over the bf16 probabilities the MFMA consumes
-//    (v_dot2), and the O rescale is skipped when no lane's running max
-//    changed.
+//  * Offset softmax in the log2 domain (scores scaled by log2(e)/sqrt(D)):
+//    each query keeps one offset for its whole key range, the maximum of its
+//    scores in the range's first tile, so later tiles need neither a running
+//    maximum nor a rescale of O; with Q pre-scaled the offset enters the
+//    score product's start value and P = 2^S costs one exponential per
+//    score.  The row sum is taken over the bf16 probabilities the MFMA
+//    consumes (v_dot2).  A range whose row sums leave the safe range (scores
+//    spread too far for one offset) is recomputed with the running-max
+//    softmax, which skips the O rescale when no lane's maximum moved.
 //  * Segment edges: tiles start on a 64-row boundary; keys outside the
 //    segment get score -inf and their V^T elements are cleared in LDS.
 #include <math.h>
