@@ -622,6 +622,27 @@ def bench_graph(args, torch, swa):
     res["host_enqueue_ms_per_step"] = {"captured": round(host_graph, 4), "eager": round(host_eager, 4)}
     res["roofline"] = _mfma_roofline(flops, ms)
     res["roofline"]["note"] = "whole captured step (12 x append, attention, merge) against the attention FLOPs"
+    if not args.no_cpu:
+        # layers are independent caches: the oracle steps one layer's cache
+        # (the same frame re-appended every step, as in the captured step)
+        from oracle import CacheConfig, NaiveRingCache
+
+        def make():
+            def st(oc, t, f, timed):
+                q, k, v = f
+                oc.append(t, k, v, True)
+                oc.evict()
+                if timed:
+                    oc.attend(q)
+                return sum(p[4] for p in oc.visible_pages())
+            return NaiveRingCache(CacheConfig(P=P, sliding_window_size=W, scale_frames=S)), st
+
+        frame0 = frame_qkv(9, 0, P, H, D)
+        tf, n, dt = _oracle_stream_rate(make, lambda t: frame0, S + W, 8,
+                                        lambda keys: 4.0 * D * H * P * keys, budget_s=10.0)
+        res["cpu_baseline"] = _cpu(tf, "TFLOP/s", f"{n} steady-state layer steps of one layer's cache (append, evict, "
+                                                  f"attend over {keys} keys each; the captured step runs {L} such "
+                                                  f"layers), {dt:.2f} s in float64 NumPy")
     return res
 
 
